@@ -1,0 +1,222 @@
+"""Plain, slow, float64 CPU oracle for causal grouped-query attention with QK-RMSNorm + RoPE.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check of the graft entry module and the CPU
+baseline leg of the benchmark may import this module. The product path (the HIP library and
+its Python binding) never calls it, and this module imports nothing from that path.
+
+Every function is the plain definition written out in NumPy float64, following the pages:
+
+* zhanghao0806.com, "Qwen3系列1-理论基础&真实结构" (below: "Qwen3 series 1"), sections D1-2
+  (stable softmax), D1-4 (scaled dot-product attention), D1-5 (causal mask), D2-1 (RMSNorm),
+  D2-2 (QK-Norm, then RoPE; the block-diagonal rotation matrix R(pos)), D2-3 (GQA groups,
+  KV cache, prefill and decode).
+* ewbang.com, "深入剖析Qwen3模型架构" (below: "Qwen3 architecture"), section 3.1.2 (GQA module
+  that repeat-interleaves K/V heads; RoPE on adjacent element pairs) and section 3.4.1 (RoPE
+  inverse frequencies base^(-2j/d) with base 1e6).
+* selfknow.cn, nano-vllm "Qwen3" page, "Attention 的 Forward 流程" steps (4) q_norm/k_norm,
+  (5) rotary embedding, (6) attention reading and writing the KV cache.
+
+Readings taken where the pages are silent (each also listed in the design notes):
+norm before RoPE; RMSNorm with a learned weight (not L2 normalisation); eps inside the square
+root; one weight vector shared by all Q heads and one by all K heads; rotation of adjacent
+pairs (2j, 2j+1), counter-clockwise; angles in float64; positions feed RoPE only while the
+causal mask uses the index inside the sequence; query head i uses KV head floor(i / h);
+decode's seq_lens[b] counts the new token, whose K/V are in the cache before attention.
+
+Every function here is pinned by the ``-m "not gpu"`` tests (closed forms, the pages'
+properties, brute force on tiny inputs and a library special case).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------- RMSNorm
+def rms_norm(x: np.ndarray, gamma: np.ndarray | None, eps: float) -> np.ndarray:
+    """gamma * x / sqrt(mean(x^2) + eps) over the last axis.
+
+    Qwen3 series 1, D2-1 (RMSNorm formula: no centring, eps inside the root, learned gamma);
+    D2-2 (applied per head to Q and to K after projection; one gamma for all Q heads and one
+    for all K heads). ``gamma=None`` skips the norm."""
+    x = np.asarray(x, dtype=np.float64)
+    if gamma is None:
+        return x.copy()
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return np.asarray(gamma, dtype=np.float64) * (x / np.sqrt(ms + eps))
+
+
+# ----------------------------------------------------------------------------- RoPE
+def rope_inv_freq(d: int, theta: float) -> np.ndarray:
+    """omega_j = theta^(-2j/d), j = 0..d/2-1 (Qwen3 architecture, 3.4.1; base 1e6)."""
+    j = np.arange(d // 2, dtype=np.float64)
+    return np.power(float(theta), -2.0 * j / d)
+
+
+def rope(x: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray:
+    """Rotate each adjacent pair (x_2j, x_2j+1) of x[t, head, :] counter-clockwise by
+    positions[t] * omega_j.
+
+    Qwen3 series 1, D2-2 (R(pos) is block-diagonal with 2x2 rotation blocks
+    [[cos, -sin], [sin, cos]] of angle pos*theta_j); Qwen3 architecture, 3.1.2 (pairs are
+    the even/odd elements, rotated as a complex product). ``theta == 0`` skips RoPE."""
+    x = np.asarray(x, dtype=np.float64)
+    if theta == 0:
+        return x.copy()
+    d = x.shape[-1]
+    phi = np.asarray(positions, dtype=np.float64)[:, None] * rope_inv_freq(d, theta)[None, :]
+    c = np.cos(phi)[:, None, :]
+    s = np.sin(phi)[:, None, :]
+    a = x[..., 0::2]
+    b = x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = a * c - b * s
+    y[..., 1::2] = a * s + b * c
+    return y
+
+
+def qk_norm_rope(q, k, positions, q_norm_w, k_norm_w, eps, theta):
+    """Prologue: per-head RMSNorm of Q (gamma_q) and K (gamma_k), then RoPE at positions.
+
+    nano-vllm "Qwen3" page, forward steps (4) then (5); Qwen3 series 1, D2-2. V is neither
+    normalised nor rotated. q: [N, H, d], k: [N, G, d], positions: [N]."""
+    qt = rope(rms_norm(q, q_norm_w, eps), positions, theta)
+    kt = rope(rms_norm(k, k_norm_w, eps), positions, theta)
+    return qt, kt
+
+
+# ----------------------------------------------------------------------------- attention core
+def _scale(d: int, scale: float | None) -> float:
+    # Qwen3 series 1, D1-4: scores are divided by sqrt(d_k).
+    return 1.0 / np.sqrt(d) if not scale else float(scale)
+
+
+def softmax_rows(S: np.ndarray) -> np.ndarray:
+    """Row softmax with the row maximum subtracted first (Qwen3 series 1, D1-2).
+    Entries equal to -inf get weight exactly 0 (D1-5)."""
+    m = np.max(S, axis=-1, keepdims=True)
+    E = np.exp(S - m)
+    return E / np.sum(E, axis=-1, keepdims=True)
+
+
+def attention_weights(qt_i: np.ndarray, kt_g: np.ndarray, causal: bool, scale=None):
+    """P = softmax(q k^T / sqrt(d) + M) for one query head against its KV head.
+
+    Qwen3 series 1, D1-4 (formula softmax(QK^T/sqrt(d_k) + M)); D1-5 (M is -inf where the
+    key index exceeds the query index). qt_i: [Tq, d], kt_g: [Tk, d]; with causal masking
+    query row r sits at key index r + (Tk - Tq)."""
+    Tq, d = qt_i.shape
+    Tk = kt_g.shape[0]
+    S = (qt_i @ kt_g.T) * _scale(d, scale)
+    if causal:
+        r = np.arange(Tq)[:, None] + (Tk - Tq)
+        c = np.arange(Tk)[None, :]
+        S = np.where(c > r, -np.inf, S)
+    return softmax_rows(S)
+
+
+def attend(qt: np.ndarray, kt: np.ndarray, v: np.ndarray, causal: bool, scale=None):
+    """Grouped-query attention over one sequence.
+
+    qt: [T, H, d]; kt, v: [T, G, d]. Query head i uses KV head g = floor(i / h), h = H / G:
+    the mapping of repeating every K/V head h times along the head axis (Qwen3 architecture,
+    3.1.2; Qwen3 series 1, D2-3). Each head: P V with P from ``attention_weights``."""
+    T, H, d = qt.shape
+    G = kt.shape[1]
+    if H % G:
+        raise ValueError("H must be a multiple of G")
+    h = H // G
+    out = np.empty((T, H, d), dtype=np.float64)
+    for i in range(H):
+        g = i // h
+        P = attention_weights(qt[:, i, :], kt[:, g, :], causal, scale)
+        out[:, i, :] = P @ v[:, g, :]
+    return out
+
+
+# ----------------------------------------------------------------------------- prefill
+def prefill(q, k, v, positions, cu_seqlens, q_norm_w, k_norm_w, eps, theta, causal=True,
+            scale=None):
+    """Packed prefill: prologue on every token, then attention inside each sequence.
+
+    q: [N, H, d]; k, v: [N, G, d]; positions: [N]; cu_seqlens: [B+1] offsets. The causal
+    mask uses the index inside the sequence; positions feed RoPE only."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    qt, kt = qk_norm_rope(q, k, positions, q_norm_w, k_norm_w, eps, theta)
+    out = np.zeros_like(q)
+    for b in range(len(cu_seqlens) - 1):
+        s, e = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
+        if e > s:
+            out[s:e] = attend(qt[s:e], kt[s:e], v[s:e], causal, scale)
+    return out
+
+
+def prefill_rows(q, k, v, positions, cu_seqlens, rows, q_norm_w, k_norm_w, eps, theta,
+                 causal=True, scale=None):
+    """Selected output rows of ``prefill``: rows are packed token indices. Each row is the
+    same definition evaluated for that query token alone (its full score row over the
+    visible keys of its sequence). Returns [len(rows), H, d]."""
+    rows = np.asarray(rows, dtype=np.int64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    H, d = q.shape[1], q.shape[2]
+    G = k.shape[1]
+    h = H // G
+    out = np.empty((len(rows), H, d), dtype=np.float64)
+    seq_of = np.searchsorted(cu, rows, side="right") - 1
+    kt_cache = {}
+    for n, (t, b) in enumerate(zip(rows, seq_of)):
+        s, e = int(cu[b]), int(cu[b + 1])
+        if b not in kt_cache:
+            kt_cache = {b: rope(rms_norm(np.asarray(k[s:e], np.float64), k_norm_w, eps),
+                                positions[s:e], theta)}
+        kt = kt_cache[b]
+        qt = rope(rms_norm(np.asarray(q[t:t + 1], np.float64), q_norm_w, eps),
+                  positions[t:t + 1], theta)[0]
+        r = int(t - s)
+        hi = r + 1 if causal else e - s
+        vb = np.asarray(v[s:s + hi], np.float64)
+        for i in range(H):
+            g = i // h
+            p = attention_weights(qt[i:i + 1], kt[:hi, g, :], False, scale)[0]
+            out[n, i, :] = p @ vb[:, g, :]
+    return out
+
+
+# ----------------------------------------------------------------------------- decode
+def decode_one(q_b, k_rows, v_rows, seq_len, q_norm_w, k_norm_w, eps, theta, position=None,
+               k_new=None, v_new=None, scale=None):
+    """Single-token decode of one sequence.
+
+    q_b: [H, d] raw query of the new token; k_rows, v_rows: [>= seq_len, G, d] cache rows,
+    K taken as already normalised and rotated (the cache holds post-prologue K and raw V,
+    nano-vllm "Qwen3" page step (6) after (5)). The new token sits at slot p = seq_len - 1
+    (or ``position``): if k_new/v_new [G, d] are given, RoPE(RMSNorm(k_new)) and v_new are
+    placed there before attention (Qwen3 series 1, D2-3: each layer writes its K/V into the
+    cache before computing attention). The single query sees every cached row 0..seq_len-1.
+    Returns (out [H, d], k_slot, v_slot) where the slots are the appended rows or None."""
+    L = int(seq_len)
+    H, d = q_b.shape
+    if L == 0:
+        return np.zeros((H, d)), None, None
+    slot = L - 1
+    pos = slot if position is None else int(position)
+    kc = np.array(k_rows[:L], dtype=np.float64)
+    vc = np.array(v_rows[:L], dtype=np.float64)
+    k_slot = v_slot = None
+    if k_new is not None:
+        k_slot = rope(rms_norm(np.asarray(k_new, np.float64)[None], k_norm_w, eps),
+                      np.array([pos]), theta)[0]
+        v_slot = np.asarray(v_new, np.float64)
+        kc[slot] = k_slot
+        vc[slot] = v_slot
+    qt = rope(rms_norm(np.asarray(q_b, np.float64)[None], q_norm_w, eps), np.array([pos]),
+              theta)[0]
+    G = kc.shape[1]
+    h = H // G
+    out = np.empty((H, d))
+    for i in range(H):
+        g = i // h
+        p = attention_weights(qt[i:i + 1], kc[:, g, :], False, scale)[0]
+        out[i] = p @ vc[:, g, :]
+    return out, k_slot, v_slot

@@ -1,0 +1,266 @@
+"""Seeded synthetic inputs for causal grouped-query attention (QK-RMSNorm + RoPE).
+
+This module only draws numbers and encodes them in the storage dtype. It holds none of the
+attention arithmetic, so both the fp64 CPU oracle (under ``oracle/``) and the HIP path can
+take their inputs from here without sharing any of the method's code.
+
+Recipe (the pages measure nothing at the kernel level, so the inputs stand in for
+post-projection Q/K/V activations at Qwen3 head shapes):
+
+* Generator: ``numpy.random.default_rng`` (PCG64). Every draw is float32, then encoded in the
+  case dtype (bf16 by round-to-nearest-even on the fp32 bit pattern; fp32 as drawn).
+* Prefill draw order from ``default_rng(seed)``: sequence lengths (if drawn), q, k, v, then
+  gamma_q and gamma_k (U(0.5, 1.5), or exactly 1).
+* Decode draw order from ``default_rng(seed)``: lengths, q, k_new, v_new, gamma_q, gamma_k.
+  The cache rows of sequence b come from their own stream ``default_rng([seed, b])`` (K rows
+  then V rows), so one sequence can be regenerated on its own.
+* Values are N(0, 1); positions restart at 0 in every packed sequence.
+"""
+from __future__ import annotations
+
+import concurrent.futures as _cf
+import dataclasses
+import os
+
+import numpy as np
+
+F32 = "f32"
+BF16 = "bf16"
+
+
+# ----------------------------------------------------------------------------- encodings
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even); returns uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact decode of bf16 bit patterns to float64."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def encode(x_f32: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == BF16:
+        return f32_to_bf16_bits(x_f32)
+    if dtype == F32:
+        return np.ascontiguousarray(x_f32, dtype=np.float32)
+    raise ValueError(dtype)
+
+
+def to_f64(stored: np.ndarray, dtype: str) -> np.ndarray:
+    """The exact values a stored array holds, as float64."""
+    if dtype == BF16:
+        return bf16_bits_to_f64(stored)
+    if dtype == F32:
+        return np.asarray(stored, dtype=np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def _normal(rng, shape):
+    return rng.standard_normal(size=shape, dtype=np.float32)
+
+
+def _gamma(rng, d, kind):
+    if kind == "ones":
+        return np.ones(d, dtype=np.float32)
+    if kind == "uniform":
+        return rng.uniform(0.5, 1.5, size=d).astype(np.float32)
+    raise ValueError(kind)
+
+
+# ----------------------------------------------------------------------------- prefill
+@dataclasses.dataclass
+class PrefillCase:
+    """Packed (token-major) prefill inputs. Arrays are in storage form: float32 for f32
+    cases, uint16 bf16 bit patterns for bf16 cases."""
+
+    name: str
+    seed: int
+    dtype: str
+    lengths: np.ndarray  # int64 [B]
+    H: int
+    G: int
+    d: int
+    causal: bool
+    eps: float
+    theta: float
+    q: np.ndarray  # [N, H, d]
+    k: np.ndarray  # [N, G, d]
+    v: np.ndarray  # [N, G, d]
+    q_norm_w: np.ndarray  # [d]
+    k_norm_w: np.ndarray  # [d]
+    positions: np.ndarray  # int32 [N]
+    cu_seqlens: np.ndarray  # int32 [B + 1]
+
+    @property
+    def B(self) -> int:
+        return int(self.lengths.shape[0])
+
+    @property
+    def N(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    @property
+    def T_max(self) -> int:
+        return int(self.lengths.max()) if self.B else 0
+
+    @property
+    def dense(self) -> bool:
+        """All sequences share one length, so the batch can be passed as [B, T, ...]."""
+        return bool(self.B > 0 and np.all(self.lengths == self.lengths[0]))
+
+    def f64(self, name: str) -> np.ndarray:
+        return to_f64(getattr(self, name), self.dtype)
+
+    @property
+    def flops(self) -> float:
+        """Algorithmic FLOPs: 4*d*H per visible (query, key) pair (2d for QK^T, 2d for PV)."""
+        L = self.lengths.astype(np.float64)
+        pairs = np.sum(L * (L + 1) / 2) if self.causal else np.sum(L * L)
+        return float(4.0 * self.d * self.H * pairs)
+
+
+def default_positions(lengths: np.ndarray) -> np.ndarray:
+    """Positions 0..T_b-1 inside each packed sequence."""
+    if len(lengths) == 0:
+        return np.zeros(0, dtype=np.int32)
+    return np.concatenate([np.arange(int(t), dtype=np.int32) for t in lengths]).astype(np.int32)
+
+
+def cu_seqlens_of(lengths: np.ndarray) -> np.ndarray:
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))]).astype(np.int32)
+
+
+def make_prefill(name, seed, lengths=None, H=16, G=8, d=128, dtype=BF16, causal=True,
+                 gamma="uniform", eps=1e-6, theta=1e6, length_range=None, n_seqs=None,
+                 positions=None) -> PrefillCase:
+    """Draw one prefill case. Either ``lengths`` is given, or ``n_seqs`` lengths are drawn
+    uniformly from the integer range ``length_range`` (inclusive) first."""
+    rng = np.random.default_rng(seed)
+    if lengths is None:
+        lo, hi = length_range
+        lengths = rng.integers(lo, hi + 1, size=n_seqs)
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cu = cu_seqlens_of(lengths)
+    N = int(cu[-1])
+    q = encode(_normal(rng, (N, H, d)), dtype)
+    k = encode(_normal(rng, (N, G, d)), dtype)
+    v = encode(_normal(rng, (N, G, d)), dtype)
+    gq = encode(_gamma(rng, d, gamma), dtype)
+    gk = encode(_gamma(rng, d, gamma), dtype)
+    pos = default_positions(lengths) if positions is None else np.asarray(positions, np.int32)
+    return PrefillCase(name=name, seed=seed, dtype=dtype, lengths=lengths, H=H, G=G, d=d,
+                       causal=causal, eps=eps, theta=theta, q=q, k=k, v=v, q_norm_w=gq,
+                       k_norm_w=gk, positions=pos, cu_seqlens=cu)
+
+
+# ----------------------------------------------------------------------------- decode
+@dataclasses.dataclass
+class DecodeCase:
+    """Single-token decode against a contiguous per-sequence cache [B, max_seq, G, d].
+
+    ``seq_lens[b]`` counts the new token: its K/V sit (or are appended) at slot
+    seq_lens[b]-1 before attention. Cache rows are produced on demand by ``cache_rows``."""
+
+    name: str
+    seed: int
+    dtype: str
+    seq_lens: np.ndarray  # int32 [B]
+    max_seq: int
+    H: int
+    G: int
+    d: int
+    eps: float
+    theta: float
+    q: np.ndarray  # [B, H, d]
+    k_new: np.ndarray  # [B, G, d]
+    v_new: np.ndarray  # [B, G, d]
+    q_norm_w: np.ndarray
+    k_norm_w: np.ndarray
+
+    @property
+    def B(self) -> int:
+        return int(self.seq_lens.shape[0])
+
+    def f64(self, name: str) -> np.ndarray:
+        return to_f64(getattr(self, name), self.dtype)
+
+    def cache_rows(self, b: int):
+        """(k_rows, v_rows) of sequence b, each [seq_lens[b], G, d] in storage form."""
+        L = int(self.seq_lens[b])
+        rng = np.random.default_rng([self.seed, b])
+        k = encode(_normal(rng, (L, self.G, self.d)), self.dtype)
+        v = encode(_normal(rng, (L, self.G, self.d)), self.dtype)
+        return k, v
+
+    def iter_cache_rows(self, threads: int | None = None):
+        """Yield (b, k_rows, v_rows) for every sequence, drawn on a thread pool."""
+        threads = threads or min(16, len(os.sched_getaffinity(0)))
+        with _cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            futs = {ex.submit(self.cache_rows, b): b for b in range(self.B)}
+            for f in _cf.as_completed(futs):
+                k, v = f.result()
+                yield futs[f], k, v
+
+    @property
+    def kv_bytes(self) -> float:
+        """Algorithmic decode bytes: visible K and V rows, plus q in and out."""
+        el = 2 if self.dtype == BF16 else 4
+        kv = float(np.sum(self.seq_lens.astype(np.float64))) * self.G * self.d * 2 * el
+        return kv + 2.0 * self.B * self.H * self.d * el
+
+
+def make_decode(name, seed, B=64, len_range=(1024, 32768), max_seq=32768, H=32, G=8, d=128,
+                dtype=BF16, gamma="uniform", eps=1e-6, theta=1e6, seq_lens=None) -> DecodeCase:
+    rng = np.random.default_rng(seed)
+    if seq_lens is None:
+        lo, hi = len_range
+        seq_lens = rng.integers(lo, hi + 1, size=B)
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    assert seq_lens.max(initial=0) <= max_seq
+    q = encode(_normal(rng, (B, H, d)), dtype)
+    k_new = encode(_normal(rng, (B, G, d)), dtype)
+    v_new = encode(_normal(rng, (B, G, d)), dtype)
+    gq = encode(_gamma(rng, d, gamma), dtype)
+    gk = encode(_gamma(rng, d, gamma), dtype)
+    return DecodeCase(name=name, seed=seed, dtype=dtype, seq_lens=seq_lens, max_seq=max_seq,
+                      H=H, G=G, d=d, eps=eps, theta=theta, q=q, k_new=k_new, v_new=v_new,
+                      q_norm_w=gq, k_norm_w=gk)
+
+
+# ----------------------------------------------------------------------------- named workloads
+def tiny_f32():
+    """Tiny fp32 prefill: B=1, T=128, H=16, G=8, d=64, causal, gamma = 1."""
+    return make_prefill("tiny_f32_T128_H16_G8_d64", 1, lengths=[128], H=16, G=8, d=64,
+                        dtype=F32, gamma="ones")
+
+
+def prefill_4k():
+    """bf16 prefill: B=1, T=4096, H=16, G=8, d=128, causal, gamma ~ U(0.5, 1.5)."""
+    return make_prefill("bf16_prefill_T4096_H16_G8_d128", 2, lengths=[4096], H=16, G=8, d=128)
+
+
+def prefill_varlen():
+    """bf16 packed prefill: 8 sequences, T_b ~ U{512..8192}, H=32, G=8, d=128."""
+    return make_prefill("bf16_varlen_8x[512,8192]_H32_G8_d128", 3, length_range=(512, 8192),
+                        n_seqs=8, H=32, G=8, d=128)
+
+
+def decode_64():
+    """bf16 decode: 64 sequences x 1 new token, L_b ~ U{1024..32768}, H=32, G=8, d=128."""
+    return make_decode("bf16_decode_64x[1024,32768]_H32_G8_d128", 4)
+
+
+def prefill_long(G=4):
+    """bf16 long prefill: B=1, T=32768, H=64, G=4 (h=16) or G=1 (MQA), d=128."""
+    seed = 5 if G == 4 else 6
+    return make_prefill(f"bf16_prefill_T32768_H64_G{G}_d128", seed, lengths=[32768], H=64,
+                        G=G, d=128)
