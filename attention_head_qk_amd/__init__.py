@@ -1,0 +1,194 @@
+"""Causal grouped-query attention with QK-RMSNorm + RoPE on MI355X (gfx950).
+
+Thin torch-facing binding of libgqa.so (include/gqa.h): it checks shapes, passes
+``tensor.data_ptr()`` values and the current torch stream to the C ABI, and allocates the
+workspace and outputs with torch when the caller does not pass them. Every step of the
+computation runs in the library's HIP kernels; nothing here computes attention, and there is
+no fallback when the library is missing (importing raises).
+
+    out = prefill(q, k, v)                       # q [B, T, H, d], k/v [B, T, G, d]
+    out = prefill(q, k, v, cu_seqlens=cu, max_seqlen=Tmax)   # packed q [N, H, d]
+    out = decode(q, k_cache, v_cache, seq_lens)  # q [B, H, d], caches [B, S, G, d]
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import GqaError  # noqa: F401
+
+_lib.load()  # fail at import, loudly, if the HIP library is not built
+
+__all__ = ["prefill", "decode", "qk_norm_rope", "workspace_bytes", "decode_split_keys",
+           "GqaError"]
+
+_DTYPES = {torch.float32: _lib.GQA_F32, torch.bfloat16: _lib.GQA_BF16}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _params(dtype, q_norm_w, k_norm_w, eps, theta, scale, stream, device):
+    p = _lib.default_params()
+    p.dtype = _DTYPES[dtype]
+    p.q_norm_w = _ptr(_dev(q_norm_w, "q_norm_w", dtype))
+    p.k_norm_w = _ptr(_dev(k_norm_w, "k_norm_w", dtype))
+    p.eps = float(eps)
+    p.rope_theta = float(theta)
+    p.scale = float(scale)
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    p.stream = ctypes.c_void_p(s.cuda_stream)
+    return p
+
+
+def workspace_bytes(op: str, B: int, T_or_max_seq: int, H: int, G: int, d: int,
+                    dtype=torch.bfloat16) -> int:
+    code = {"prefill": _lib.GQA_OP_PREFILL, "decode": _lib.GQA_OP_DECODE}[op]
+    return int(_lib.load().gqa_workspace_bytes(code, B, T_or_max_seq, H, G, d, _DTYPES[dtype]))
+
+
+def decode_split_keys() -> int:
+    return int(_lib.load().gqa_decode_split_keys())
+
+
+def _prof(p, prof):
+    """prof = (start, stop) torch.cuda.Event pair recorded around the main kernel."""
+    if prof is None:
+        return
+    start, stop = prof
+    for ev in (start, stop):
+        if not ev.cuda_event:  # torch creates the HIP event on its first record
+            ev.record()
+    p.prof_start = ctypes.c_void_p(start.cuda_event)
+    p.prof_stop = ctypes.c_void_p(stop.cuda_event)
+
+
+def _workspace(ws, nbytes, device):
+    if ws is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    _dev(ws, "workspace")
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    return ws
+
+
+def prefill(q, k, v, positions=None, *, causal=True, q_norm_w=None, k_norm_w=None, eps=1e-6,
+            theta=1e6, scale=0.0, cu_seqlens=None, max_seqlen=None, k_out=None, out=None,
+            workspace=None, stream=None, prof=None):
+    """gqa_prefill. Dense: q [B, T, H, d], k/v [B, T, G, d]. Packed: q [N, H, d], k/v
+    [N, G, d] with cu_seqlens (device int32 [B+1]) and max_seqlen >= every length.
+    positions: optional device int32 [N] (RoPE positions; default 0..T_b-1 per sequence).
+    k_out: optional [N, G, d] receiving the normalised, rotated K. prof: optional
+    (start, stop) torch.cuda.Event pair recorded around the attention kernel alone.
+    Returns out like q."""
+    _dev(q, "q")
+    dtype = q.dtype
+    _dev(k, "k", dtype)
+    _dev(v, "v", dtype)
+    if cu_seqlens is None:
+        if q.dim() != 4:
+            raise ValueError("dense prefill takes q [B, T, H, d]")
+        B, T, H, d = q.shape
+        G = k.shape[2]
+        if k.shape != (B, T, G, d) or v.shape != k.shape:
+            raise ValueError("k and v must be [B, T, G, d]")
+    else:
+        _dev(cu_seqlens, "cu_seqlens", torch.int32)
+        if q.dim() != 3 or max_seqlen is None:
+            raise ValueError("packed prefill takes q [N, H, d] and max_seqlen")
+        N, H, d = q.shape
+        G = k.shape[1]
+        B = cu_seqlens.numel() - 1
+        T = int(max_seqlen)
+        if k.shape != (N, G, d) or v.shape != k.shape:
+            raise ValueError("k and v must be [N, G, d]")
+    _dev(positions, "positions", torch.int32)
+    _dev(k_out, "k_out", dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", dtype)
+    p = _params(dtype, q_norm_w, k_norm_w, eps, theta, scale, stream, q.device)
+    nbytes = workspace_bytes("prefill", B, T, H, G, d, dtype)
+    ws = _workspace(workspace, nbytes, q.device)
+    p.workspace = _ptr(ws)
+    p.workspace_bytes = ws.numel() * ws.element_size()
+    p.cu_seqlens = _ptr(cu_seqlens)
+    p.k_out = _ptr(k_out)
+    _prof(p, prof)
+    rc = _lib.load().gqa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(positions), _ptr(out), B, T,
+                                 H, G, d, 1 if causal else 0, ctypes.byref(p))
+    _lib.check(rc, "gqa_prefill")
+    return out
+
+
+def decode(q, k_cache, v_cache, seq_lens, *, k_new=None, v_new=None, positions=None,
+           q_norm_w=None, k_norm_w=None, eps=1e-6, theta=1e6, scale=0.0, out=None,
+           workspace=None, stream=None, prof=None):
+    """gqa_decode. q [B, H, d]; caches [B, max_seq, G, d] (K post-prologue, V raw);
+    seq_lens device int32 [B] counting the new token; optional k_new/v_new [B, G, d] are
+    normalised/rotated (K) and written at slot seq_lens[b]-1 first. prof: optional
+    (start, stop) torch.cuda.Event pair recorded around the split-KV pass alone.
+    Returns out [B, H, d]."""
+    _dev(q, "q")
+    dtype = q.dtype
+    _dev(k_cache, "k_cache", dtype)
+    _dev(v_cache, "v_cache", dtype)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    _dev(k_new, "k_new", dtype)
+    _dev(v_new, "v_new", dtype)
+    _dev(positions, "positions", torch.int32)
+    B, H, d = q.shape
+    _, S, G, d2 = k_cache.shape
+    if d2 != d or v_cache.shape != k_cache.shape or k_cache.shape[0] != B:
+        raise ValueError("caches must be [B, max_seq, G, d]")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", dtype)
+    p = _params(dtype, q_norm_w, k_norm_w, eps, theta, scale, stream, q.device)
+    nbytes = workspace_bytes("decode", B, S, H, G, d, dtype)
+    ws = _workspace(workspace, nbytes, q.device)
+    p.workspace = _ptr(ws)
+    p.workspace_bytes = ws.numel() * ws.element_size()
+    p.k_new = _ptr(k_new)
+    p.v_new = _ptr(v_new)
+    p.positions = _ptr(positions)
+    _prof(p, prof)
+    rc = _lib.load().gqa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                _ptr(out), B, H, G, d, S, ctypes.byref(p))
+    _lib.check(rc, "gqa_decode")
+    return out
+
+
+def qk_norm_rope(q, k=None, positions=None, *, q_norm_w=None, k_norm_w=None, eps=1e-6,
+                 theta=1e6, q_out=None, k_out=None, stream=None):
+    """gqa_qk_norm_rope: q [N, H, d] (and k [N, G, d]) -> normalised, rotated copies.
+    positions: device int32 [N] or None for 0..N-1."""
+    _dev(q, "q")
+    dtype = q.dtype
+    N, H, d = q.shape
+    G = 1 if k is None else k.shape[1]
+    _dev(k, "k", dtype)
+    _dev(positions, "positions", torch.int32)
+    q_out = torch.empty_like(q) if q_out is None else _dev(q_out, "q_out", dtype)
+    if k is not None:
+        k_out = torch.empty_like(k) if k_out is None else _dev(k_out, "k_out", dtype)
+    p = _params(dtype, q_norm_w, k_norm_w, eps, theta, 0.0, stream, q.device)
+    rc = _lib.load().gqa_qk_norm_rope(_ptr(q), _ptr(k), _ptr(positions), _ptr(q_out),
+                                      _ptr(k_out), N, H, G, d, ctypes.byref(p))
+    _lib.check(rc, "gqa_qk_norm_rope")
+    return q_out, k_out

@@ -1,0 +1,139 @@
+// Device-side helpers shared by the gfx950 kernels of libgqa: vector types, bf16 packing,
+// wave-level shuffles and the kernel argument blocks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// bf16 is carried as raw 16-bit patterns in memory.
+typedef uint16_t bf16_t;
+
+constexpr int kMaxHalfD = 64;  // d <= 128
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Two fp32 values to one packed bf16 pair (low half = a), round to nearest even
+// (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2_t v = {a, b};
+  bf16x2_t r = __builtin_convertvector(v, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Unpack 8 bf16 (one 16-byte chunk) to fp32.
+__device__ __forceinline__ void unpack8(const u32x4_t w, float x[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = lo_bf16(w[i]);
+    x[2 * i + 1] = hi_bf16(w[i]);
+  }
+}
+
+__device__ __forceinline__ u32x4_t pack8(const float x[8]) {
+  u32x4_t w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+  return w;
+}
+
+// Element loads/stores of 8 consecutive values in either storage type.
+__device__ __forceinline__ void load8(const float* p, float x[8]) {
+  const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
+  const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = a[i];
+    x[4 + i] = b[i];
+  }
+}
+__device__ __forceinline__ void load8(const bf16_t* p, float x[8]) {
+  unpack8(*reinterpret_cast<const u32x4_t*>(p), x);
+}
+__device__ __forceinline__ void store8(float* p, const float x[8]) {
+  f32x4_t a, b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = x[i];
+    b[i] = x[4 + i];
+  }
+  *reinterpret_cast<f32x4_t*>(p) = a;
+  *reinterpret_cast<f32x4_t*>(p + 4) = b;
+}
+__device__ __forceinline__ void store8(bf16_t* p, const float x[8]) {
+  *reinterpret_cast<u32x4_t*>(p) = pack8(x);
+}
+
+__device__ __forceinline__ float xor_shfl(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// Sum over aligned groups of W consecutive lanes (W a power of two <= 64).
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < W; m <<= 1) v += xor_shfl(v, m);
+  return v;
+}
+
+// ---------------------------------------------------------------------------- kernel args
+struct PrologueArgs {
+  const void* q;      // rows to normalise and rotate with gamma_q   [rows, H, D]
+  const void* k;      // rows to normalise and rotate with gamma_k   [rows, G, D] or null
+  const void* v;      // decode only: V rows copied into the cache    [B, G, D] or null
+  void* q_out;        // [rows, H, D]
+  void* k_out;        // prefill: [N, G, D]; decode: K cache [B, max_seq, G, D]
+  void* v_out;        // decode: V cache
+  const int32_t* positions;
+  const int32_t* cu_seqlens;  // prefill, packed
+  const int32_t* seq_lens;    // decode
+  const void* gq;
+  const void* gk;
+  float eps;
+  int decode;         // 0: token rows (prefill / stand-alone), 1: one row per sequence
+  int B, T, H, G;
+  int max_seq;
+  int use_rope;
+  double omega[kMaxHalfD];  // theta^(-2j/d), computed on the host in fp64
+};
+
+struct PrefillArgs {
+  const void* qt;     // [N, H, D] normalised, rotated Q
+  const void* kt;     // [N, G, D] normalised, rotated K
+  const void* v;      // [N, G, D]
+  void* out;          // [N, H, D]
+  const int32_t* cu_seqlens;  // null: dense, sequence b = tokens [b*T, (b+1)*T)
+  int B, T, H, G, h;
+  int causal;
+  int n_blk;          // column blocks of the longest sequence
+  float scale;        // score scale (1/sqrt(d) by default)
+  float scale_log2e;  // scale * log2(e)
+};
+
+struct DecodeArgs {
+  const void* qt;     // [B, H, D] normalised, rotated query
+  const void* k_cache;
+  const void* v_cache;  // [B, max_seq, G, D]
+  const int32_t* seq_lens;
+  float* part_o;      // [B, H, nsplit, D]
+  float* part_ml;     // [B, H, nsplit, 2]  (running max in log2 units, sum)
+  void* out;          // [B, H, D]
+  int B, H, G, h, max_seq, nsplit;
+  float scale_log2e;
+};
+
+constexpr int kDecodeSplit = 512;  // keys per split of the decode pass
+
+}  // namespace gqa

@@ -1,0 +1,286 @@
+// Host side of the libgqa C ABI (include/gqa.h): argument checks, workspace layout, launch
+// geometry and the dtype / head-dim dispatch. Every check runs before the first HIP call, so
+// a rejected call enqueues nothing and touches no device.
+#include <cmath>
+#include <cstdint>
+
+#include "gqa.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxHeads = 4096;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_size(int dtype) { return dtype == GQA_BF16 ? 2 : 4; }
+
+bool dtype_ok(int dtype) { return dtype == GQA_F32 || dtype == GQA_BF16; }
+
+int decode_nsplit(int max_seq) {
+  return max_seq <= 0 ? 0 : (max_seq + gqa::kDecodeSplit - 1) / gqa::kDecodeSplit;
+}
+
+// Checks shared by every entry point. Returns GQA_OK or the first failure.
+gqa_status check_heads(int H, int G, int d) {
+  if (H <= 0 || G <= 0 || H > kMaxHeads || G > kMaxHeads || H % G != 0) return GQA_EINVAL;
+  if (d != 64 && d != 128) return GQA_ENOTSUP;
+  return GQA_OK;
+}
+
+gqa_status check_params(const gqa_params* p) {
+  if (!p) return GQA_EINVAL;
+  if (!dtype_ok(p->dtype)) return GQA_ENOTSUP;
+  if (!(p->eps >= 0.f) || !std::isfinite(p->eps)) return GQA_EINVAL;
+  if (!(p->scale >= 0.f) || !std::isfinite(p->scale)) return GQA_EINVAL;
+  if (!(p->rope_theta >= 0.0) || !std::isfinite(p->rope_theta)) return GQA_EINVAL;
+  if (!aligned(p->q_norm_w, 16) || !aligned(p->k_norm_w, 16)) return GQA_EINVAL;
+  return GQA_OK;
+}
+
+bool tensor_ok(const void* t) { return t != nullptr && aligned(t, 16); }
+bool opt_tensor_ok(const void* t) { return aligned(t, 16); }
+bool opt_int_ok(const void* t) { return aligned(t, 4); }
+
+float eff_scale(const gqa_params* p, int d) {
+  return p->scale > 0.f ? p->scale : (float)(1.0 / std::sqrt((double)d));
+}
+
+void fill_rope(gqa::PrologueArgs& a, const gqa_params* p, int d) {
+  a.use_rope = p->rope_theta > 0.0 ? 1 : 0;
+  for (int j = 0; j < gqa::kMaxHalfD; ++j)
+    a.omega[j] = (a.use_rope && j < d / 2) ? std::pow(p->rope_theta, -2.0 * j / d) : 0.0;
+}
+
+gqa_status from_hip(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_EHIP; }
+
+// Records the caller's optional profiling event on the stream.
+hipError_t mark(void* ev, hipStream_t s) {
+  return ev ? hipEventRecord(reinterpret_cast<hipEvent_t>(ev), s) : hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+void gqa_params_init(gqa_params* p) {
+  if (!p) return;
+  p->dtype = GQA_BF16;
+  p->q_norm_w = nullptr;
+  p->k_norm_w = nullptr;
+  p->eps = 1e-6f;
+  p->rope_theta = 1e6;
+  p->scale = 0.f;
+  p->cu_seqlens = nullptr;
+  p->k_out = nullptr;
+  p->k_new = nullptr;
+  p->v_new = nullptr;
+  p->positions = nullptr;
+  p->workspace = nullptr;
+  p->workspace_bytes = 0;
+  p->stream = nullptr;
+  p->prof_start = nullptr;
+  p->prof_stop = nullptr;
+}
+
+const char* gqa_status_str(gqa_status s) {
+  switch (s) {
+    case GQA_OK: return "GQA_OK: success";
+    case GQA_EINVAL: return "GQA_EINVAL: invalid argument";
+    case GQA_ENOTSUP: return "GQA_ENOTSUP: unsupported head dim or dtype";
+    case GQA_EWORKSPACE: return "GQA_EWORKSPACE: workspace missing or too small";
+    case GQA_EHIP: return "GQA_EHIP: HIP launch error";
+  }
+  return "unknown gqa_status";
+}
+
+int gqa_decode_split_keys(void) { return gqa::kDecodeSplit; }
+
+size_t gqa_workspace_bytes(int op, int B, int T_or_max_seq, int H, int G, int d, int dtype) {
+  if (B < 0 || T_or_max_seq < 0 || check_heads(H, G, d) != GQA_OK || !dtype_ok(dtype)) return 0;
+  const size_t es = elem_size(dtype);
+  if (op == GQA_OP_PREFILL) {
+    const size_t N = (size_t)B * (size_t)T_or_max_seq;
+    return align_up(N * H * d * es) + align_up(N * G * d * es);
+  }
+  if (op == GQA_OP_DECODE) {
+    const size_t ns = (size_t)decode_nsplit(T_or_max_seq);
+    return align_up((size_t)B * H * d * es) + align_up((size_t)B * H * ns * d * 4) +
+           align_up((size_t)B * H * ns * 2 * 4);
+  }
+  return 0;
+}
+
+gqa_status gqa_prefill(const void* q, const void* k, const void* v, const int32_t* positions,
+                       void* out, int B, int T, int H, int G, int d, int causal,
+                       const gqa_params* p) {
+  gqa_status st = check_params(p);
+  if (st != GQA_OK) return st;
+  if ((st = check_heads(H, G, d)) != GQA_OK) return st;
+  if (B < 0 || T < 0 || (causal != 0 && causal != 1)) return GQA_EINVAL;
+  if ((long long)B * T > 0x7fffffffLL) return GQA_EINVAL;
+  if (B == 0 || T == 0) return GQA_OK;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(out)) return GQA_EINVAL;
+  if (!opt_int_ok(positions) || !opt_int_ok(p->cu_seqlens) || !opt_tensor_ok(p->k_out))
+    return GQA_EINVAL;
+  const size_t need = gqa_workspace_bytes(GQA_OP_PREFILL, B, T, H, G, d, p->dtype);
+  if (!p->workspace || !aligned(p->workspace, 16) || p->workspace_bytes < need)
+    return GQA_EWORKSPACE;
+
+  const bool bf16 = p->dtype == GQA_BF16;
+  const size_t es = elem_size(p->dtype);
+  const size_t N = (size_t)B * T;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(p->stream);
+  char* ws = static_cast<char*>(p->workspace);
+  void* qt = ws;
+  void* kt = p->k_out ? p->k_out : ws + align_up(N * H * d * es);
+  (void)hipGetLastError();
+
+  gqa::PrologueArgs pa{};
+  pa.q = q;
+  pa.k = k;
+  pa.q_out = qt;
+  pa.k_out = kt;
+  pa.positions = positions;
+  pa.cu_seqlens = p->cu_seqlens;
+  pa.gq = p->q_norm_w;
+  pa.gk = p->k_norm_w;
+  pa.eps = p->eps;
+  pa.decode = 0;
+  pa.B = B;
+  pa.T = T;
+  pa.H = H;
+  pa.G = G;
+  fill_rope(pa, p, d);
+  if ((st = from_hip(gqa::launch_prologue(pa, B * T, d, bf16, stream))) != GQA_OK) return st;
+
+  gqa::PrefillArgs fa{};
+  fa.qt = qt;
+  fa.kt = kt;
+  fa.v = v;
+  fa.out = out;
+  fa.cu_seqlens = p->cu_seqlens;
+  fa.B = B;
+  fa.T = T;
+  fa.H = H;
+  fa.G = G;
+  fa.h = H / G;
+  fa.causal = causal;
+  const long cols = (long)T * fa.h;
+  const int cpb = gqa::prefill_bf16_cols_per_block();
+  fa.n_blk = (int)((cols + cpb - 1) / cpb);
+  fa.scale = eff_scale(p, d);
+  fa.scale_log2e = (float)((double)fa.scale * 1.4426950408889634074);
+  if ((st = from_hip(mark(p->prof_start, stream))) != GQA_OK) return st;
+  st = from_hip(bf16 ? gqa::launch_prefill_bf16(fa, d, stream)
+                     : gqa::launch_prefill_f32(fa, d, stream));
+  if (st != GQA_OK) return st;
+  return from_hip(mark(p->prof_stop, stream));
+}
+
+gqa_status gqa_decode(const void* q, void* k_cache, void* v_cache, const int32_t* seq_lens,
+                      void* out, int B, int H, int G, int d, int max_seq,
+                      const gqa_params* p) {
+  gqa_status st = check_params(p);
+  if (st != GQA_OK) return st;
+  if ((st = check_heads(H, G, d)) != GQA_OK) return st;
+  if (B < 0 || max_seq < 0) return GQA_EINVAL;
+  if (B == 0) return GQA_OK;
+  if (max_seq == 0) return GQA_EINVAL;
+  if (!tensor_ok(q) || !tensor_ok(k_cache) || !tensor_ok(v_cache) || !tensor_ok(out))
+    return GQA_EINVAL;
+  if (!seq_lens || !opt_int_ok(seq_lens) || !opt_int_ok(p->positions)) return GQA_EINVAL;
+  if ((p->k_new == nullptr) != (p->v_new == nullptr)) return GQA_EINVAL;
+  if (!opt_tensor_ok(p->k_new) || !opt_tensor_ok(p->v_new)) return GQA_EINVAL;
+  const size_t need = gqa_workspace_bytes(GQA_OP_DECODE, B, max_seq, H, G, d, p->dtype);
+  if (!p->workspace || !aligned(p->workspace, 16) || p->workspace_bytes < need)
+    return GQA_EWORKSPACE;
+
+  const bool bf16 = p->dtype == GQA_BF16;
+  const size_t es = elem_size(p->dtype);
+  const int ns = decode_nsplit(max_seq);
+  hipStream_t stream = reinterpret_cast<hipStream_t>(p->stream);
+  char* ws = static_cast<char*>(p->workspace);
+  void* qt = ws;
+  float* part_o = reinterpret_cast<float*>(ws + align_up((size_t)B * H * d * es));
+  float* part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(part_o) +
+                                            align_up((size_t)B * H * ns * d * 4));
+  (void)hipGetLastError();
+
+  gqa::PrologueArgs pa{};
+  pa.q = q;
+  pa.k = p->k_new;
+  pa.v = p->v_new;
+  pa.q_out = qt;
+  pa.k_out = k_cache;
+  pa.v_out = v_cache;
+  pa.positions = p->positions;
+  pa.seq_lens = seq_lens;
+  pa.gq = p->q_norm_w;
+  pa.gk = p->k_norm_w;
+  pa.eps = p->eps;
+  pa.decode = 1;
+  pa.B = B;
+  pa.T = 1;
+  pa.H = H;
+  pa.G = G;
+  pa.max_seq = max_seq;
+  fill_rope(pa, p, d);
+  if ((st = from_hip(gqa::launch_prologue(pa, B, d, bf16, stream))) != GQA_OK) return st;
+
+  gqa::DecodeArgs da{};
+  da.qt = qt;
+  da.k_cache = k_cache;
+  da.v_cache = v_cache;
+  da.seq_lens = seq_lens;
+  da.part_o = part_o;
+  da.part_ml = part_ml;
+  da.out = out;
+  da.B = B;
+  da.H = H;
+  da.G = G;
+  da.h = H / G;
+  da.max_seq = max_seq;
+  da.nsplit = ns;
+  da.scale_log2e = (float)((double)eff_scale(p, d) * 1.4426950408889634074);
+  if ((st = from_hip(mark(p->prof_start, stream))) != GQA_OK) return st;
+  if ((st = from_hip(gqa::launch_decode_split(da, d, bf16, stream))) != GQA_OK) return st;
+  if ((st = from_hip(mark(p->prof_stop, stream))) != GQA_OK) return st;
+  return from_hip(gqa::launch_decode_combine(da, d, bf16, stream));
+}
+
+gqa_status gqa_qk_norm_rope(const void* q, const void* k, const int32_t* positions,
+                            void* q_out, void* k_out, int N, int H, int G, int d,
+                            const gqa_params* p) {
+  gqa_status st = check_params(p);
+  if (st != GQA_OK) return st;
+  if ((st = check_heads(H, G, d)) != GQA_OK) return st;
+  if (N < 0) return GQA_EINVAL;
+  if (N == 0) return GQA_OK;
+  if (!tensor_ok(q) || !tensor_ok(q_out)) return GQA_EINVAL;
+  if ((k == nullptr) != (k_out == nullptr)) return GQA_EINVAL;
+  if (!opt_tensor_ok(k) || !opt_tensor_ok(k_out) || !opt_int_ok(positions)) return GQA_EINVAL;
+  (void)hipGetLastError();
+  gqa::PrologueArgs pa{};
+  pa.q = q;
+  pa.k = k;
+  pa.q_out = q_out;
+  pa.k_out = k_out;
+  pa.positions = positions;
+  pa.gq = p->q_norm_w;
+  pa.gk = p->k_norm_w;
+  pa.eps = p->eps;
+  pa.decode = 0;
+  pa.B = 1;
+  pa.T = N;
+  pa.H = H;
+  pa.G = G;
+  fill_rope(pa, p, d);
+  return from_hip(gqa::launch_prologue(pa, N, d, p->dtype == GQA_BF16,
+                                       reinterpret_cast<hipStream_t>(p->stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the causal GQA hot path (QK-RMSNorm + RoPE prologue, prefill attention,
+decode split-KV + combine) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload default|...]
+
+A step of the default workload is one pass of the whole path over one batch of synthetic
+input: gqa_prefill on the bf16 prefill T=4096, H=16, G=8, d=128 (causal, gamma ~ U(0.5,1.5),
+theta 1e6), then gqa_decode on 64 sequences x 1 new token with cache lengths U{1024..32768},
+H=32, G=8, d=128 (the new token's K/V appended first). Inputs are resident in HBM before the
+timed region. Prints one JSON line:
+
+* value: prefill TFLOP/s of the whole gqa_prefill call (prologue + attention), algorithmic
+  FLOPs 4*d*H*sum T_b(T_b+1)/2; ``decode`` carries the decode GB/s of the whole gqa_decode
+  call, algorithmic bytes = visible K and V rows + q + out.
+* roofline: the prefill attention kernel alone (HIP events recorded by the library right
+  around its launch, on the launch stream), against the 2.5 PFLOP/s bf16 dense MFMA peak;
+  roofline_decode: the decode split-KV kernel alone against 8 TB/s HBM.
+* cpu_baseline: the fp64 CPU oracle timed on the GPU machine's host on a bounded sample of the
+  same prefill workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
+HBM_PEAK_GBS = 8000.0
+
+WORKLOADS = ("default", "tiny_f32", "prefill_4k", "varlen", "decode", "long_g4", "long_g1")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_case(name):
+    import workloads as W
+    return {"tiny_f32": W.tiny_f32, "prefill_4k": W.prefill_4k, "default": W.prefill_4k,
+            "varlen": W.prefill_varlen, "long_g4": lambda: W.prefill_long(4),
+            "long_g1": lambda: W.prefill_long(1)}[name]()
+
+
+class Prefill:
+    def __init__(self, case):
+        import torch
+        import attention_head_qk_amd as gqa
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from _gpu import device_prefill_inputs
+        self.case = case
+        self.dev = device_prefill_inputs(case)
+        self.gqa = gqa
+        c = case
+        self.ws = torch.empty(gqa.workspace_bytes("prefill", c.B, max(c.T_max, 1), c.H, c.G, c.d,
+                                                  self.dev["q"].dtype), dtype=torch.uint8,
+                              device="cuda")
+        self.out = torch.empty_like(self.dev["q"])
+
+    def __call__(self, prof=None):
+        c, dv = self.case, self.dev
+        kw = dict(causal=c.causal, q_norm_w=dv["q_norm_w"], k_norm_w=dv["k_norm_w"], eps=c.eps,
+                  theta=c.theta, workspace=self.ws, prof=prof)
+        if c.dense:
+            B, T = c.B, c.T_max
+            return self.gqa.prefill(dv["q"].view(B, T, c.H, c.d), dv["k"].view(B, T, c.G, c.d),
+                                    dv["v"].view(B, T, c.G, c.d), dv["positions"],
+                                    out=self.out.view(B, T, c.H, c.d), **kw)
+        return self.gqa.prefill(dv["q"], dv["k"], dv["v"], dv["positions"], cu_seqlens=dv["cu"],
+                                max_seqlen=c.T_max, out=self.out, **kw)
+
+    @property
+    def work(self):
+        return self.case.flops
+
+
+class Decode:
+    def __init__(self, case):
+        import torch
+        import attention_head_qk_amd as gqa
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from _gpu import device_decode_inputs
+        self.case = case
+        self.dev = device_decode_inputs(case)
+        self.gqa = gqa
+        c = case
+        self.ws = torch.empty(gqa.workspace_bytes("decode", c.B, c.max_seq, c.H, c.G, c.d),
+                              dtype=torch.uint8, device="cuda")
+        self.out = torch.empty_like(self.dev["q"])
+
+    def __call__(self, prof=None):
+        c, dv = self.case, self.dev
+        return self.gqa.decode(dv["q"], dv["k_cache"], dv["v_cache"], dv["seq_lens"],
+                               k_new=dv["k_new"], v_new=dv["v_new"], q_norm_w=dv["q_norm_w"],
+                               k_norm_w=dv["k_norm_w"], eps=c.eps, theta=c.theta,
+                               workspace=self.ws, out=self.out, prof=prof)
+
+    @property
+    def work(self):
+        return self.case.kv_bytes
+
+
+def cpu_baseline(case, budget_s=12.0):
+    """Time the fp64 oracle (as it stands) on whole query heads of the prefill workload,
+    head after head, until about ``budget_s`` seconds of CPU work; report TFLOP/s over the
+    algorithmic FLOPs of the heads done."""
+    import numpy as np
+    from oracle import gqa_oracle as O
+    try:
+        import threadpoolctl
+        cores = max(i["num_threads"] for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:
+        cores = os.cpu_count() or 1
+    q, k, v = case.f64("q"), case.f64("k"), case.f64("v")
+    gq, gk = case.f64("q_norm_w"), case.f64("k_norm_w")
+    t0 = time.perf_counter()
+    qt, kt = O.qk_norm_rope(q, k, case.positions, gq, gk, case.eps, case.theta)
+    h = case.H // case.G
+    heads = 0
+    L = case.lengths.astype(np.float64)
+    per_head = 4.0 * case.d * float(np.sum(L * (L + 1) / 2 if case.causal else L * L))
+    while heads < case.H and (time.perf_counter() - t0) < budget_s:
+        i = heads
+        for b in range(case.B):
+            s, e = int(case.cu_seqlens[b]), int(case.cu_seqlens[b + 1])
+            P = O.attention_weights(qt[s:e, i], kt[s:e, i // h], case.causal)
+            _ = P @ v[s:e, i // h]
+        heads += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(per_head * heads / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"fp64 NumPy oracle on {heads} of {case.H} query heads of {case.name} "
+                      f"(prologue on all tokens + full score matrix per head), {dt:.1f} s"}
+
+
+def timed(fn, steps, warmup):
+    """Warm up, then time ``steps`` calls with events around each whole call and around the
+    main kernel (recorded by the library on the launch stream)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for e in ev:
+        for x in e:
+            x.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record()
+        fn(prof=(e[1], e[2]))
+        e[3].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = sum(e[0].elapsed_time(e[3]) for e in ev) / steps
+    kern_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    return wall, call_ms, kern_ms
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=WORKLOADS, default="default")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads as W
+    log(f"bench: workload={args.workload} steps={args.steps} warmup={args.warmup}")
+    torch.cuda.init()
+    dev_name = torch.cuda.get_device_name(0)
+
+    pre = dec = None
+    if args.workload != "decode":
+        pre = Prefill(prefill_case(args.workload))
+        log(f"bench: prefill inputs ready ({pre.case.name}, N={pre.case.N})")
+    if args.workload in ("default", "decode"):
+        dec = Decode(W.decode_64())
+        log(f"bench: decode inputs ready ({dec.case.name}, sum L={int(dec.case.seq_lens.sum())})")
+    torch.cuda.synchronize()
+
+    def step(prof=None):
+        if pre is not None:
+            pre(prof)
+        if dec is not None:
+            dec()
+
+    # whole-step wall clock (both calls), events per call and per main kernel
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    log(f"bench: {args.steps} steps, {step_ms:.3f} ms/step")
+
+    res = {}
+    if pre is not None:
+        _, call_ms, kern_ms = timed(pre, args.steps, 1)
+        res["prefill"] = (call_ms, kern_ms)
+        log(f"bench: prefill call {call_ms:.4f} ms, attention kernel {kern_ms:.4f} ms")
+    if dec is not None:
+        _, call_ms, kern_ms = timed(dec, args.steps, 1)
+        res["decode"] = (call_ms, kern_ms)
+        log(f"bench: decode call {call_ms:.4f} ms, split kernel {kern_ms:.4f} ms")
+
+    line = {"metric": "GQA prefill TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "data": "synthetic", "device": dev_name}
+    cfg = {}
+    if pre is not None:
+        c = pre.case
+        call_ms, kern_ms = res["prefill"]
+        tf_call = pre.work / (call_ms * 1e-3) / 1e12
+        tf_kern = pre.work / (kern_ms * 1e-3) / 1e12
+        peak = FP32_PEAK_TFLOPS if c.dtype == W.F32 else MFMA_BF16_PEAK_TFLOPS
+        line.update({"value": round(tf_call, 3), "unit": "TFLOP/s",
+                     "dtype": "f32" if c.dtype == W.F32 else "bf16"})
+        line["roofline"] = {"bound": "mfma", "achieved": round(tf_kern, 3), "peak": peak,
+                            "unit": "TFLOP/s", "frac": round(tf_kern / peak, 4), "traffic": None,
+                            "kernel": "prefill_bf16_kernel" if c.dtype == W.BF16 else "prefill_f32_kernel",
+                            "kernel_ms": round(kern_ms, 5), "flops_per_launch": c.flops}
+        line["prefill"] = {"ms": round(call_ms, 5), "tflops": round(tf_call, 3),
+                           "frac_of_peak": round(tf_call / peak, 4)}
+        cfg["prefill"] = {"name": c.name, "B": c.B, "lengths_sum": c.N, "T_max": c.T_max, "H": c.H,
+                          "G": c.G, "d": c.d, "causal": c.causal, "seed": c.seed}
+    if dec is not None:
+        c = dec.case
+        call_ms, kern_ms = res["decode"]
+        gbs_call = dec.work / (call_ms * 1e-3) / 1e9
+        gbs_kern = dec.work / (kern_ms * 1e-3) / 1e9
+        line["decode"] = {"value": round(gbs_call, 2), "unit": "GB/s", "ms": round(call_ms, 5),
+                          "frac_of_peak": round(gbs_call / HBM_PEAK_GBS, 4),
+                          "bytes": dec.work}
+        line["roofline_decode"] = {"bound": "hbm", "achieved": round(gbs_kern, 2),
+                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": round(gbs_kern / HBM_PEAK_GBS, 4), "traffic": None,
+                                   "kernel": "decode_split_kernel", "kernel_ms": round(kern_ms, 5)}
+        cfg["decode"] = {"name": c.name, "B": c.B, "sum_L": int(c.seq_lens.sum()), "max_seq": c.max_seq,
+                         "H": c.H, "G": c.G, "d": c.d, "seed": c.seed}
+        if pre is None:
+            line.update({"value": round(gbs_call, 2), "unit": "GB/s", "dtype": "bf16",
+                         "roofline": line.pop("roofline_decode")})
+    names = [v["name"] for v in cfg.values()]
+    line["config"] = {"workload": " + ".join(names), **cfg}
+    if not args.no_cpu_baseline and pre is not None:
+        log("bench: timing the CPU oracle")
+        line["cpu_baseline"] = cpu_baseline(pre.case)
+    elif not args.no_cpu_baseline:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,146 @@
+/*
+ * gqa.h -- C ABI of the MI355X (gfx950) causal grouped-query attention library (libgqa.so).
+ *
+ * The operation (one transformer attention layer between the QKV projection and o_proj):
+ *
+ *   1. QK prologue.  For every token t and head: x_hat = x / sqrt(mean(x^2) + eps),
+ *      x_bar = gamma (.) x_hat, then RoPE: each adjacent pair (x_2j, x_2j+1) is rotated
+ *      counter-clockwise by pos[t] * omega_j, omega_j = theta^(-2j/d).  Applied to Q with
+ *      gamma_q and to K with gamma_k; V is left alone.
+ *        - RMSNorm: zhanghao0806.com "Qwen3系列1-理论基础&真实结构", D2-1 (formula).
+ *        - per head, Q and K only, norm then RoPE, one gamma for all Q heads and one for
+ *          all K heads: same page, D2-2; nano-vllm "Qwen3" page (selfknow.cn), Attention
+ *          forward steps (4) and (5).
+ *        - R(pos) as 2x2 rotation blocks: same page, D2-2 (matrix R(pos)); adjacent
+ *          even/odd pairs: ewbang.com "深入剖析Qwen3模型架构", 3.1.2 (RoPE code);
+ *          omega_j and base 1e6: same article, 3.4.1.
+ *   2. Attention.  Query head i reads KV head g = floor(i / h), h = H / G (the article's
+ *      3.1.2 GQA module repeats each K/V head h times); for each sequence
+ *      out = softmax(Q K^T * scale + M) V with M = -inf where key index > query index
+ *      (causal) and the row maximum subtracted inside the softmax.
+ *        - zhanghao0806.com page, D1-4 (formula), D1-5 (causal mask), D1-2 (stable
+ *          softmax), D2-3 (groups, KV cache, prefill / decode).
+ *   Decode: one new token per sequence attends to all seq_lens[b] cached rows; its own K/V
+ *   are written into the cache first (D2-3: the layer writes K/V into the cache before
+ *   computing attention).
+ *
+ * Conventions for every entry point
+ *   - Tensors are contiguous, row-major, token-major and live in device memory:
+ *       q, out [N, H, d]; k, v [N, G, d]; decode q, out [B, H, d];
+ *       caches [B, max_seq, G, d] holding K after norm + RoPE and raw V.
+ *     Element type is params->dtype (fp32 or bf16) for q, k, v, out, caches, k_new, v_new,
+ *     k_out and the two norm weights.  Integer arrays are device int32.
+ *   - The caller owns all memory.  The library allocates nothing and keeps no state
+ *     between calls, so it is re-entrant.  Work is enqueued on params->stream (a
+ *     hipStream_t; NULL = the default stream) and the call returns without waiting.
+ *     Buffers must stay valid until that stream work has finished.  Outputs must not
+ *     alias inputs.
+ *   - Errors found on the host are returned at once and nothing is enqueued:
+ *       GQA_EINVAL    null required pointer, negative size, H, G or d <= 0, H % G != 0,
+ *                     a device pointer not 16-byte aligned, an int array not 4-byte aligned;
+ *       GQA_ENOTSUP   d not in {64, 128}, or an unknown dtype;
+ *       GQA_EWORKSPACE workspace smaller than gqa_workspace_bytes() or NULL when needed;
+ *       GQA_EHIP      a HIP launch error.
+ *     A batch with B == 0 or T == 0 is valid and enqueues nothing.  Device faults show up
+ *     at the caller's next synchronisation.  Values inside device int arrays (positions,
+ *     seq_lens, cu_seqlens) are trusted: out-of-range values are undefined behaviour,
+ *     except a sequence of length 0 (no rows; decode writes zeros).  Nothing is printed and
+ *     no C++ exception crosses this interface.
+ *   - NaN or Inf inputs propagate to the outputs they touch.
+ */
+#ifndef GQA_H
+#define GQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gqa_status {
+  GQA_OK = 0,
+  GQA_EINVAL = 1,
+  GQA_ENOTSUP = 2,
+  GQA_EWORKSPACE = 3,
+  GQA_EHIP = 4
+} gqa_status;
+
+typedef enum gqa_dtype { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
+
+typedef enum gqa_op { GQA_OP_PREFILL = 0, GQA_OP_DECODE = 1, GQA_OP_QK_NORM_ROPE = 2 } gqa_op;
+
+typedef struct gqa_params {
+  gqa_dtype dtype;           /* element type of every float tensor of the call              */
+  const void *q_norm_w;      /* [d] gamma_q; NULL = no RMSNorm on Q                          */
+  const void *k_norm_w;      /* [d] gamma_k; NULL = no RMSNorm on K                          */
+  float eps;                 /* RMSNorm epsilon, added inside the square root                */
+  double rope_theta;         /* RoPE base theta (Qwen3: 1e6); 0 = no RoPE                    */
+  float scale;               /* score scale; 0 = 1/sqrt(d)                                   */
+  const int32_t *cu_seqlens; /* prefill: device [B+1] packed offsets, cu[0] = 0;
+                                NULL = dense, every sequence has length T                   */
+  void *k_out;               /* prefill: optional [N, G, d] output of normalised, rotated K
+                                (e.g. the KV cache); NULL = keep it in the workspace         */
+  const void *k_new;         /* decode: optional [B, G, d] raw K of the new token            */
+  const void *v_new;         /* decode: optional [B, G, d] V of the new token; with k_new,
+                                RoPE(RMSNorm(k_new)) and v_new are written into cache slot
+                                seq_lens[b]-1 before attention                               */
+  const int32_t *positions;  /* decode: optional device [B] RoPE positions of the new
+                                tokens; NULL = seq_lens[b]-1                                 */
+  void *workspace;           /* device scratch, >= gqa_workspace_bytes(), 256-byte aligned  */
+  size_t workspace_bytes;
+  void *stream;              /* hipStream_t; NULL = default stream                           */
+  void *prof_start;          /* optional hipEvent_t, recorded on the stream right before the
+                                main kernel (prefill attention, or the decode split pass);
+                                for callers that time that kernel alone. NULL = none       */
+  void *prof_stop;           /* optional hipEvent_t, recorded right after that kernel       */
+} gqa_params;
+
+/* Fills p with defaults: bf16, no norm weights, eps 1e-6, theta 1e6, scale 1/sqrt(d),
+ * dense, no workspace, default stream, no profiling events. */
+void gqa_params_init(gqa_params *p);
+
+/* Prefill (prompt) attention with the QK prologue.
+ *   q [N, H, d], k and v [N, G, d] raw projections; out [N, H, d].
+ *   positions: device [N] RoPE positions, or NULL for 0..T_b-1 inside every sequence (the
+ *     causal mask always uses the index inside the sequence; positions feed RoPE only).
+ *   Dense: N = B*T and sequence b is tokens [b*T, (b+1)*T).  Packed: p->cu_seqlens given,
+ *     N = cu_seqlens[B], sequence b is [cu[b], cu[b+1]) and T must be >= every length.
+ *   causal: 1 = causal mask inside each sequence, 0 = every key of the sequence visible.
+ *   Needs p->workspace of gqa_workspace_bytes(GQA_OP_PREFILL, B, T, H, G, d, dtype). */
+gqa_status gqa_prefill(const void *q, const void *k, const void *v, const int32_t *positions,
+                       void *out, int B, int T, int H, int G, int d, int causal,
+                       const gqa_params *p);
+
+/* Single-token decode against a contiguous KV cache.
+ *   q [B, H, d] raw query of the new token per sequence; out [B, H, d].
+ *   k_cache, v_cache [B, max_seq, G, d]: rows 0..seq_lens[b]-1 are visible to sequence b;
+ *     K rows are post-prologue.  With p->k_new and p->v_new the new row is written at
+ *     slot seq_lens[b]-1 first (so k_cache and v_cache are written only then).
+ *   seq_lens: device [B], 0 <= seq_lens[b] <= max_seq, counting the new token.
+ *   Needs p->workspace of gqa_workspace_bytes(GQA_OP_DECODE, B, max_seq, H, G, d, dtype). */
+gqa_status gqa_decode(const void *q, void *k_cache, void *v_cache, const int32_t *seq_lens,
+                      void *out, int B, int H, int G, int d, int max_seq,
+                      const gqa_params *p);
+
+/* The QK prologue alone (RMSNorm then RoPE), for step-level checks.
+ *   q [N, H, d] -> q_out [N, H, d]; k [N, G, d] -> k_out [N, G, d]; positions device [N]
+ *   or NULL for 0..N-1.  No workspace. */
+gqa_status gqa_qk_norm_rope(const void *q, const void *k, const int32_t *positions,
+                            void *q_out, void *k_out, int N, int H, int G, int d,
+                            const gqa_params *p);
+
+/* Bytes of workspace an entry point needs (0 when none).  op is a gqa_op, T_or_max_seq is
+ * T for prefill and max_seq for decode, dtype a gqa_dtype.  Returns 0 for invalid sizes. */
+size_t gqa_workspace_bytes(int op, int B, int T_or_max_seq, int H, int G, int d, int dtype);
+
+/* Keys per split of the decode pass (the split-KV partition of each sequence). */
+int gqa_decode_split_keys(void);
+
+/* Static text for a status code. */
+const char *gqa_status_str(gqa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GQA_H */

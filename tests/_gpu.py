@@ -1,0 +1,145 @@
+"""Helpers shared by the GPU tests: move seeded inputs to the device, call the HIP path
+through the binding, bring results back as float64, and compare with the tolerances the
+path is held to (fp32: max abs <= 1e-5; bf16: max abs <= 2e-2 and mean abs <= 2e-3)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import workloads as W
+
+F32_MAX_ABS = 1e-5
+BF16_MAX_ABS = 2e-2
+BF16_MEAN_ABS = 2e-3
+
+
+def say(*a):
+    """Name the case on stdout before a GPU step, so a fault can be traced to it."""
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(arr: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == W.BF16:
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.cuda()
+
+
+def i32(arr) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.int32)).cuda()
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check(got: np.ndarray, want: np.ndarray, dtype: str, what: str = "") -> dict:
+    err = np.abs(got - want)
+    stats = {"max_abs": float(err.max(initial=0.0)), "mean_abs": float(err.mean()) if err.size else 0.0}
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    if dtype == W.F32:
+        assert stats["max_abs"] <= F32_MAX_ABS, f"{what}: {stats}"
+    else:
+        assert stats["max_abs"] <= BF16_MAX_ABS and stats["mean_abs"] <= BF16_MEAN_ABS, f"{what}: {stats}"
+    return stats
+
+
+def device_prefill_inputs(case: W.PrefillCase):
+    dt = case.dtype
+    return dict(q=to_dev(case.q, dt), k=to_dev(case.k, dt), v=to_dev(case.v, dt),
+                q_norm_w=to_dev(case.q_norm_w, dt), k_norm_w=to_dev(case.k_norm_w, dt),
+                positions=i32(case.positions), cu=i32(case.cu_seqlens))
+
+
+def run_prefill(case: W.PrefillCase, dev=None, packed=None, pass_positions=True, **kw):
+    """Run gqa_prefill on a case; packed=None picks dense for one-length batches."""
+    import attention_head_qk_amd as gqa
+    dev = dev or device_prefill_inputs(case)
+    if packed is None:
+        packed = not case.dense
+    pos = dev["positions"] if pass_positions else None
+    common = dict(causal=case.causal, q_norm_w=dev["q_norm_w"], k_norm_w=dev["k_norm_w"],
+                  eps=case.eps, theta=case.theta, **kw)
+    if packed:
+        out = gqa.prefill(dev["q"], dev["k"], dev["v"], pos, cu_seqlens=dev["cu"],
+                          max_seqlen=max(case.T_max, 1), **common)
+    else:
+        B, T = case.B, case.T_max
+        H, G, d = case.H, case.G, case.d
+        out = gqa.prefill(dev["q"].view(B, T, H, d), dev["k"].view(B, T, G, d),
+                          dev["v"].view(B, T, G, d), pos, **common).view(-1, H, d)
+    return out
+
+
+def oracle_prefill(case: W.PrefillCase):
+    from oracle import gqa_oracle as O
+    return O.prefill(case.f64("q"), case.f64("k"), case.f64("v"), case.positions,
+                     case.cu_seqlens, case.f64("q_norm_w"), case.f64("k_norm_w"), case.eps,
+                     case.theta, case.causal)
+
+
+def oracle_prefill_rows(case: W.PrefillCase, rows):
+    from oracle import gqa_oracle as O
+    return O.prefill_rows(case.f64("q"), case.f64("k"), case.f64("v"), case.positions,
+                          case.cu_seqlens, rows, case.f64("q_norm_w"), case.f64("k_norm_w"),
+                          case.eps, case.theta, case.causal)
+
+
+def sample_rows(case: W.PrefillCase, n_random: int, seed: int = 0, tile: int = 64):
+    """Packed row indices: rows 0, 1, both sides of every tile boundary below 4*tile, the
+    last row of every sequence, plus n_random seeded rows."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for b in range(case.B):
+        s, e = int(case.cu_seqlens[b]), int(case.cu_seqlens[b + 1])
+        if e == s:
+            continue
+        for r in (0, 1, tile - 1, tile, 2 * tile - 1, 2 * tile, e - s - 1, e - s - 2):
+            if 0 <= r < e - s:
+                rows.add(s + r)
+    N = case.N
+    rows.update(int(x) for x in rng.integers(0, N, size=n_random))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def device_decode_inputs(case: W.DecodeCase, fill_invalid=None):
+    """Device tensors for a decode case; the cache is [B, max_seq, G, d] with only the first
+    seq_lens[b] rows of each sequence filled (the rest zero, or ``fill_invalid``)."""
+    dt = case.dtype
+    tdt = torch.bfloat16 if dt == W.BF16 else torch.float32
+    shape = (case.B, case.max_seq, case.G, case.d)
+    kc = torch.zeros(shape, dtype=tdt, device="cuda")
+    vc = torch.zeros(shape, dtype=tdt, device="cuda")
+    if fill_invalid is not None:
+        kc.fill_(fill_invalid)
+        vc.fill_(fill_invalid)
+    for b, k, v in case.iter_cache_rows():
+        L = k.shape[0]
+        kc[b, :L] = to_dev(k, dt)
+        vc[b, :L] = to_dev(v, dt)
+    return dict(q=to_dev(case.q, dt), k_cache=kc, v_cache=vc, seq_lens=i32(case.seq_lens),
+                k_new=to_dev(case.k_new, dt), v_new=to_dev(case.v_new, dt),
+                q_norm_w=to_dev(case.q_norm_w, dt), k_norm_w=to_dev(case.k_norm_w, dt))
+
+
+def run_decode(case: W.DecodeCase, dev, append=True, positions=None, **kw):
+    import attention_head_qk_amd as gqa
+    return gqa.decode(dev["q"], dev["k_cache"], dev["v_cache"], dev["seq_lens"],
+                      k_new=dev["k_new"] if append else None,
+                      v_new=dev["v_new"] if append else None, positions=positions,
+                      q_norm_w=dev["q_norm_w"], k_norm_w=dev["k_norm_w"], eps=case.eps,
+                      theta=case.theta, **kw)
+
+
+def oracle_decode_seq(case: W.DecodeCase, b: int, append=True, position=None):
+    from oracle import gqa_oracle as O
+    k, v = case.cache_rows(b)
+    return O.decode_one(case.f64("q")[b], W.to_f64(k, case.dtype), W.to_f64(v, case.dtype),
+                        int(case.seq_lens[b]), case.f64("q_norm_w"), case.f64("k_norm_w"),
+                        case.eps, case.theta, position=position,
+                        k_new=case.f64("k_new")[b] if append else None,
+                        v_new=case.f64("v_new")[b] if append else None)

@@ -1,0 +1,132 @@
+"""The C ABI of libgqa.so on the CPU: it loads, exports every function include/gqa.h
+declares, sizes workspaces, and rejects bad arguments before any HIP call (no GPU needed:
+every call here returns from the host-side checks)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_head_qk_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa.h")
+
+# Fake device addresses: the checks only look at them, never dereference them.
+A = 0x10000
+MIS = 0x10008  # 8-byte aligned only
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[\w\s\*]*?\b(gqa_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for fn in ("gqa_prefill", "gqa_decode", "gqa_qk_norm_rope", "gqa_workspace_bytes",
+               "gqa_status_str", "gqa_params_init", "gqa_decode_split_keys"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for fn in declared_functions():
+        assert hasattr(lib, fn), fn
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_status_strings():
+    for code, tag in [(0, "GQA_OK"), (1, "GQA_EINVAL"), (2, "GQA_ENOTSUP"),
+                      (3, "GQA_EWORKSPACE"), (4, "GQA_EHIP")]:
+        assert _lib.status_str(code).startswith(tag)
+
+
+def test_params_init_defaults():
+    p = _lib.default_params()
+    assert p.dtype == _lib.GQA_BF16
+    assert abs(p.eps - 1e-6) < 1e-12 and p.rope_theta == 1e6 and p.scale == 0.0
+    assert not p.workspace and not p.stream and not p.cu_seqlens
+
+
+def test_workspace_bytes():
+    lib = _lib.load()
+    ws = lib.gqa_workspace_bytes
+    # prefill: q~ [N,H,d] and k~ [N,G,d] in the element type, each rounded up to 256 bytes
+    assert ws(_lib.GQA_OP_PREFILL, 1, 4096, 16, 8, 128, _lib.GQA_BF16) == 4096 * 24 * 128 * 2
+    assert ws(_lib.GQA_OP_PREFILL, 1, 3, 2, 1, 64, _lib.GQA_F32) == 1536 + 768
+    assert ws(_lib.GQA_OP_PREFILL, 1, 3, 1, 1, 64, _lib.GQA_BF16) == 512 + 512  # 384 -> 512
+    # decode: q~ + fp32 partial O + fp32 (m, l) per split
+    S = lib.gqa_decode_split_keys()
+    ns = -(-32768 // S)
+    want = 64 * 32 * 128 * 2 + 64 * 32 * ns * 128 * 4 + 64 * 32 * ns * 2 * 4
+    assert ws(_lib.GQA_OP_DECODE, 64, 32768, 32, 8, 128, _lib.GQA_BF16) == want
+    assert ws(_lib.GQA_OP_QK_NORM_ROPE, 4, 4, 4, 4, 128, _lib.GQA_BF16) == 0
+    assert ws(_lib.GQA_OP_PREFILL, 1, 8, 6, 4, 128, _lib.GQA_BF16) == 0  # H % G != 0
+    assert ws(_lib.GQA_OP_PREFILL, 1, 8, 8, 4, 96, _lib.GQA_BF16) == 0   # d unsupported
+
+
+def _params(**kw):
+    p = _lib.default_params()
+    p.workspace = A
+    p.workspace_bytes = 1 << 40
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def _prefill(q=A, k=A, v=A, pos=None, out=A, B=1, T=8, H=4, G=2, d=128, causal=1, **kw):
+    p = _params(**kw)
+    return _lib.load().gqa_prefill(q, k, v, pos, out, B, T, H, G, d, causal, ctypes.byref(p))
+
+
+def _decode(q=A, kc=A, vc=A, sl=A, out=A, B=2, H=4, G=2, d=128, S=16, **kw):
+    p = _params(**kw)
+    return _lib.load().gqa_decode(q, kc, vc, sl, out, B, H, G, d, S, ctypes.byref(p))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.GQA_EINVAL), (dict(k=None), _lib.GQA_EINVAL),
+    (dict(v=None), _lib.GQA_EINVAL), (dict(out=None), _lib.GQA_EINVAL),
+    (dict(q=MIS), _lib.GQA_EINVAL), (dict(out=MIS), _lib.GQA_EINVAL),
+    (dict(pos=A + 2), _lib.GQA_EINVAL),
+    (dict(H=6, G=4), _lib.GQA_EINVAL), (dict(H=0), _lib.GQA_EINVAL), (dict(G=0), _lib.GQA_EINVAL),
+    (dict(B=-1), _lib.GQA_EINVAL), (dict(T=-3), _lib.GQA_EINVAL), (dict(causal=2), _lib.GQA_EINVAL),
+    (dict(d=96), _lib.GQA_ENOTSUP), (dict(d=256), _lib.GQA_ENOTSUP),
+    (dict(dtype=7), _lib.GQA_ENOTSUP),
+    (dict(eps=-1.0), _lib.GQA_EINVAL), (dict(scale=-0.5), _lib.GQA_EINVAL),
+    (dict(rope_theta=float("nan")), _lib.GQA_EINVAL),
+    (dict(q_norm_w=A + 4), _lib.GQA_EINVAL), (dict(cu_seqlens=A + 1), _lib.GQA_EINVAL),
+    (dict(workspace=None), _lib.GQA_EWORKSPACE), (dict(workspace_bytes=100), _lib.GQA_EWORKSPACE),
+    (dict(B=0), _lib.GQA_OK), (dict(T=0), _lib.GQA_OK), (dict(B=0, q=None), _lib.GQA_OK),
+])
+def test_prefill_rejects_before_launch(kw, code):
+    assert _prefill(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.GQA_EINVAL), (dict(kc=None), _lib.GQA_EINVAL),
+    (dict(vc=MIS), _lib.GQA_EINVAL), (dict(sl=None), _lib.GQA_EINVAL),
+    (dict(sl=A + 2), _lib.GQA_EINVAL), (dict(out=None), _lib.GQA_EINVAL),
+    (dict(S=0), _lib.GQA_EINVAL), (dict(S=-1), _lib.GQA_EINVAL),
+    (dict(H=5, G=2), _lib.GQA_EINVAL), (dict(d=32), _lib.GQA_ENOTSUP),
+    (dict(k_new=A), _lib.GQA_EINVAL), (dict(v_new=A), _lib.GQA_EINVAL),
+    (dict(k_new=MIS, v_new=A), _lib.GQA_EINVAL), (dict(positions=A + 1), _lib.GQA_EINVAL),
+    (dict(workspace_bytes=10), _lib.GQA_EWORKSPACE),
+    (dict(B=0), _lib.GQA_OK), (dict(B=-2), _lib.GQA_EINVAL),
+])
+def test_decode_rejects_before_launch(kw, code):
+    assert _decode(**kw) == code
+
+
+def test_qk_norm_rope_rejects_before_launch():
+    lib = _lib.load()
+    p = _params()
+    f = lib.gqa_qk_norm_rope
+    assert f(None, None, None, A, None, 4, 4, 2, 128, ctypes.byref(p)) == _lib.GQA_EINVAL
+    assert f(A, A, None, A, None, 4, 4, 2, 128, ctypes.byref(p)) == _lib.GQA_EINVAL
+    assert f(A, None, None, A, None, 4, 4, 2, 80, ctypes.byref(p)) == _lib.GQA_ENOTSUP
+    assert f(A, None, None, A, None, -1, 4, 2, 128, ctypes.byref(p)) == _lib.GQA_EINVAL
+    assert f(A, None, None, A, None, 0, 4, 2, 128, ctypes.byref(p)) == _lib.GQA_OK
+    assert f(A, None, None, A, None, 4, 4, 2, 128, None) == _lib.GQA_EINVAL

@@ -1,0 +1,171 @@
+"""GPU parity of gqa_prefill (prologue + attention) against the fp64 oracle, element by
+element, on the seeded workloads and on ragged / degenerate shapes; plus the invariants
+that hold at any size (determinism, causality, packed = separate)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+from _gpu import (check, device_prefill_inputs, oracle_prefill, oracle_prefill_rows,
+                  run_prefill, sample_rows, say, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_f32_full():
+    case = W.tiny_f32()
+    say("prefill tiny_f32 full")
+    got = to_f64(run_prefill(case))
+    check(got, oracle_prefill(case), W.F32, case.name)
+
+
+def test_bf16_4k_full():
+    case = W.prefill_4k()
+    say("prefill bf16 T=4096 H=16 G=8 full")
+    got = to_f64(run_prefill(case))
+    stats = check(got, oracle_prefill(case), W.BF16, case.name)
+    say(case.name, stats)
+
+
+def test_varlen_packed_sampled_rows():
+    case = W.prefill_varlen()
+    say("prefill varlen packed", case.lengths.tolist())
+    got = to_f64(run_prefill(case))
+    rows = sample_rows(case, 48, seed=3)
+    check(got[rows], oracle_prefill_rows(case, rows), W.BF16, case.name)
+
+
+@pytest.mark.parametrize("G", [4, 1])
+def test_long_32k_sampled_rows(G):
+    case = W.prefill_long(G)
+    say(f"prefill long T=32768 H=64 G={G}")
+    got = to_f64(run_prefill(case))
+    rows = sample_rows(case, 24, seed=G)
+    check(got[rows], oracle_prefill_rows(case, rows), W.BF16, case.name)
+
+
+SHAPES = [
+    # (lengths, H, G, d, causal)
+    ([1], 4, 2, 128, True),
+    ([2], 2, 2, 128, True),
+    ([63], 16, 8, 128, True),
+    ([64], 16, 8, 128, True),
+    ([65], 16, 8, 128, True),
+    ([129], 12, 4, 128, True),      # h = 3: column blocks straddle positions
+    ([200], 40, 8, 128, True),      # h = 5
+    ([300], 8, 8, 128, True),       # h = 1 (MHA)
+    ([150], 64, 1, 128, True),      # MQA, h = 64
+    ([77], 128, 1, 128, True),      # h = 128: one position per column block
+    ([97], 256, 1, 128, True),      # h = 256 > columns per block
+    ([190], 16, 8, 64, True),       # d = 64
+    ([130], 32, 8, 128, False),     # no causal mask
+    ([1, 63, 64, 65, 0, 129, 7], 32, 8, 128, True),  # packed, ragged, an empty sequence
+    ([40, 0, 0, 90], 16, 4, 64, False),
+]
+
+
+@pytest.mark.parametrize("lengths,H,G,d,causal", SHAPES)
+def test_small_shapes_full(lengths, H, G, d, causal):
+    case = W.make_prefill(f"small_{lengths}_{H}_{G}_{d}_{causal}", 11 + H + G + d,
+                          lengths=lengths, H=H, G=G, d=d, causal=causal)
+    say("prefill", case.name)
+    got = to_f64(run_prefill(case))
+    check(got, oracle_prefill(case), W.BF16, case.name)
+
+
+@pytest.mark.parametrize("lengths,H,G,d,causal", [([150], 16, 8, 64, True), ([70, 0, 33], 12, 4, 128, True),
+                                                  ([100], 8, 2, 128, False)])
+def test_small_shapes_f32(lengths, H, G, d, causal):
+    case = W.make_prefill("f32_small", 5, lengths=lengths, H=H, G=G, d=d, causal=causal,
+                          dtype=W.F32)
+    say("prefill f32", lengths, H, G, d, causal)
+    check(to_f64(run_prefill(case)), oracle_prefill(case), W.F32, case.name)
+
+
+def test_peaky_softmax():
+    # gamma x 8 drives every row towards one-hot (Qwen3 series 1, D1-4 Q8); scores reach
+    # ~1e3 in magnitude. The bf16 rounding of q~ and k~ moves such a score by about |s| 2^-8
+    # (a few nats), so only rows whose oracle weight sits overwhelmingly on one key
+    # (top weight > 1 - 1e-6, i.e. a gap of > 13.8 nats) have a rounding-stable answer:
+    # there the output must be that key's V row. Every output must be finite and inside the
+    # range of V (it is a convex combination of V rows).
+    from oracle import gqa_oracle as O
+    case = W.make_prefill("peaky", 21, lengths=[257], H=8, G=2, d=128)
+    case.q_norm_w = W.encode(W.bf16_bits_to_f32(case.q_norm_w) * 8, W.BF16)
+    case.k_norm_w = W.encode(W.bf16_bits_to_f32(case.k_norm_w) * 8, W.BF16)
+    say("prefill peaky")
+    got = to_f64(run_prefill(case))
+    assert np.all(np.isfinite(got))
+    v = case.f64("v")
+    assert np.abs(got).max() <= np.abs(v).max() + 1e-2
+    qt, kt = O.qk_norm_rope(case.f64("q"), case.f64("k"), case.positions, case.f64("q_norm_w"),
+                            case.f64("k_norm_w"), case.eps, case.theta)
+    h = case.H // case.G
+    n_stable = 0
+    for i in range(case.H):
+        P = O.attention_weights(qt[:, i], kt[:, i // h], True)
+        stable = P.max(axis=1) > 1 - 1e-6
+        n_stable += int(stable.sum())
+        top = np.argmax(P, axis=1)
+        err = np.abs(got[stable, i] - v[top[stable], i // h])
+        assert err.max(initial=0.0) <= 2e-2, (i, err.max())
+    assert n_stable > case.H * 257 // 2
+
+
+def test_default_positions_and_k_out():
+    import attention_head_qk_amd as gqa
+    case = W.make_prefill("kout", 8, lengths=[70, 33], H=8, G=4, d=128)
+    dev = device_prefill_inputs(case)
+    say("prefill positions=None + k_out")
+    k_out = torch.empty_like(dev["k"])
+    a = run_prefill(case, dev=dev, pass_positions=False, k_out=k_out)
+    b = run_prefill(case, dev=dev)
+    assert torch.equal(a, b)
+    from oracle import gqa_oracle as O
+    _, kt = O.qk_norm_rope(case.f64("q"), case.f64("k"), case.positions, case.f64("q_norm_w"),
+                           case.f64("k_norm_w"), case.eps, case.theta)
+    err = np.abs(to_f64(k_out) - kt)
+    assert np.all(err <= 2.0 ** -8 * np.abs(kt) + 1e-6)
+
+
+def test_deterministic_and_causal():
+    case = W.make_prefill("inv", 31, lengths=[333], H=16, G=4, d=128)
+    dev = device_prefill_inputs(case)
+    say("prefill determinism + causality")
+    a = run_prefill(case, dev=dev)
+    b = run_prefill(case, dev=dev)
+    assert torch.equal(a, b)
+    # changing tokens from row 200 on leaves rows < 200 bit-identical
+    for name in ("q", "k", "v"):
+        dev[name][200:] = -dev[name][200:] * 1.5
+    c = run_prefill(case, dev=dev)
+    assert torch.equal(a[:200], c[:200])
+    assert not torch.equal(a[200:], c[200:])
+
+
+def test_packed_equals_separate_calls():
+    lengths = [100, 1, 64, 250]
+    case = W.make_prefill("pack", 41, lengths=lengths, H=16, G=8, d=128)
+    dev = device_prefill_inputs(case)
+    say("prefill packed vs separate")
+    packed = run_prefill(case, dev=dev, packed=True)
+    import attention_head_qk_amd as gqa
+    for b, t in enumerate(lengths):
+        s = int(case.cu_seqlens[b])
+        one = gqa.prefill(dev["q"][s:s + t][None], dev["k"][s:s + t][None],
+                          dev["v"][s:s + t][None], None, q_norm_w=dev["q_norm_w"],
+                          k_norm_w=dev["k_norm_w"], eps=case.eps, theta=case.theta)
+        assert torch.equal(one[0], packed[s:s + t])
+
+
+def test_shifted_positions_change_little():
+    # RoPE makes scores depend on position differences only: shifting every position by a
+    # constant changes outputs only by rounding (bf16 q~, k~ are re-rounded).
+    case = W.make_prefill("shift", 51, lengths=[180], H=8, G=4, d=128)
+    dev = device_prefill_inputs(case)
+    say("prefill shifted positions")
+    a = to_f64(run_prefill(case, dev=dev))
+    dev["positions"] += 1000
+    b = to_f64(run_prefill(case, dev=dev))
+    assert np.abs(a - b).max() <= 2e-2
