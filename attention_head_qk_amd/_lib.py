@@ -1,6 +1,6 @@
 """ctypes view of libgqa.so, the C ABI declared in include/gqa.h. No torch here.
 
-The library is built in-tree by ``python -m attention_head_qk_amd.build``. Loading fails
+The library is built in-tree by ``python attention_head_qk_amd/build.py``. Loading fails
 loudly (ImportError) when it is missing: there is no fallback implementation.
 """
 from __future__ import annotations
@@ -67,7 +67,7 @@ def load() -> ctypes.CDLL:
         return _LIB
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m attention_head_qk_amd.build` (needs hipcc)")
+                          "`python attention_head_qk_amd/build.py` (needs hipcc)")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         f = getattr(lib, name)

@@ -1,6 +1,9 @@
 """Build libgqa.so (the gfx950 HIP kernels and the C ABI of include/gqa.h) in-tree.
 
-Usage: python -m attention_head_qk_amd.build [--verbose] [--resource-usage]
+Usage: python attention_head_qk_amd/build.py [--verbose] [--resource-usage]
+
+(Run as a file, not as a package module: importing the package loads libgqa.so, which must
+not be required in order to rebuild it.)
 
 Every HIP source is compiled with hipcc for gfx950 only, with packed-fp32 instruction
 selection switched off (-Xclang -target-feature -Xclang -packed-fp32-ops), then linked into

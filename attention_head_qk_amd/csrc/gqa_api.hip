@@ -122,6 +122,8 @@ gqa_status gqa_prefill(const void* q, const void* k, const void* v, const int32_
   if ((st = check_heads(H, G, d)) != GQA_OK) return st;
   if (B < 0 || T < 0 || (causal != 0 && causal != 1)) return GQA_EINVAL;
   if ((long long)B * T > 0x7fffffffLL) return GQA_EINVAL;
+  // the bf16 kernel addresses one sequence's K/V rows of a group with 32-bit buffer offsets
+  if (p->dtype == GQA_BF16 && (long long)T * G * d * 2 > 0x7fffffffLL) return GQA_ENOTSUP;
   if (B == 0 || T == 0) return GQA_OK;
   if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(out)) return GQA_EINVAL;
   if (!opt_int_ok(positions) || !opt_int_ok(p->cu_seqlens) || !opt_tensor_ok(p->k_out))

@@ -38,36 +38,49 @@ namespace gqa {
 
 namespace {
 
-constexpr int KT = 64;     // keys per tile
-constexpr int COLS = 128;  // columns per workgroup (4 waves x 32)
+constexpr int KT = 64;      // keys per tile
+constexpr int COLS = 128;   // columns per workgroup (4 waves x 32)
+constexpr float TAU = 8.0f; // lazy-rescale threshold, log2 units: probabilities stay <= 2^8
+constexpr int BUF_RSRC_DW3 = 0x00020000;  // buffer descriptor word 3 for gfx9-class parts
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t w) { return __builtin_bit_cast(bf16x8_t, w); }
+
+// Wait for every outstanding vector-memory load of this wave, including LDS DMA
+// (s_waitcnt vmcnt(0); gfx9 encoding: expcnt and lgkmcnt fields left at their maxima).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// 16 bytes per lane from a buffer straight into LDS: lane i lands at lds + 16 i.
+// The builtin exists only for the device; clang's host pass drops the kernel's launch stub
+// when it sees it, so the host pass gets an empty body (it never runs device code anyway).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, const char* lds, int voff, int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)lds, 16, voff, soff, 0, 0);
+#endif
+}
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Swizzle of the 16-byte chunk index of a V^T row (8 chunks of 8 keys).
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
-
-template <int D>
-struct Tile {
-  static constexpr int DCH = D / 8;                // 16-byte chunks per K row
-  static constexpr int KROWS = 256 / DCH;          // K rows loaded per pass
-  static constexpr int KPASS = KT / KROWS;         // passes per K tile
-  static constexpr int VTHREADS = (KT / 4) * DCH;  // threads that load V (4 keys x 8 d each)
-  static constexpr int ELEMS = KT * D;             // bf16 elements per K (or V^T) tile
-};
+// Swizzle of the 16-byte chunk index of a V^T row (8 chunks of 8 keys). It depends on d mod 32
+// only, so the 32-row tiles of one lane differ by a constant offset, and it is conflict-free
+// both for the MFMA reads (16 consecutive d) and for the transposing writes (one d per 16 lanes).
+__device__ __forceinline__ int vt_swz(int d) { return ((d >> 3) & 3) ^ (d & 7); }
 
 }  // namespace
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
-  using TL = Tile<D>;
-  constexpr int DCH = TL::DCH;
-  constexpr int NST = D / 16;  // k-steps of S^T = K Q^T
-  constexpr int NMT = D / 32;  // 32-row tiles of O^T
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2][2][TL::ELEMS];  // [buf][K | V^T]
+  constexpr int DCH = D / 8;               // 16-byte chunks per K row
+  constexpr int NST = D / 16;              // k-steps of S^T = K Q^T
+  constexpr int NMT = D / 32;              // 32-row tiles of O^T
+  constexpr int KBYTES = KT * D * 2;       // one K tile
+  constexpr int VBYTES = D * KT * 2;       // one V^T tile
+  constexpr int BUFBYTES = KBYTES + VBYTES;
+  constexpr int KDMA = KBYTES / 1024 / 4;  // 1 KB DMA instructions per wave per K tile
+  constexpr int KROWS_DMA = 1024 / (D * 2);  // K rows per DMA instruction
+  __shared__ __attribute__((aligned(16))) char smem[2 * BUFBYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -108,12 +121,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   const int plim = a.causal ? pcol : 0x7fffffff;
 
   // ---- Q^T (B operand): step st holds d = 16 st + 8 grp + [0, 8) of this lane's column
-  const bf16_t* qt = reinterpret_cast<const bf16_t*>(a.qt);
-  const bf16_t* kt = reinterpret_cast<const bf16_t*>(a.kt);
-  const bf16_t* vv = reinterpret_cast<const bf16_t*>(a.v);
   bf16x8_t qf[NST];
   {
-    const bf16_t* qp = qt + ((long)(seq0 + pcol) * a.H + head) * D + 8 * grp;
+    const bf16_t* qp = reinterpret_cast<const bf16_t*>(a.qt) + ((long)(seq0 + pcol) * a.H + head) * D + 8 * grp;
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
       u32x4_t w = {0u, 0u, 0u, 0u};
@@ -122,63 +132,82 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     }
   }
 
-  // ---- tile staging: global -> registers -> LDS
-  const long kv_stride = (long)a.G * D;  // elements between consecutive tokens of K / V
-  const bf16_t* kg = kt + (long)seq0 * kv_stride + (long)g * D;
-  const bf16_t* vg = vv + (long)seq0 * kv_stride + (long)g * D;
-  const int krow0 = tid / DCH, kch = tid % DCH;
-  const bool vload = tid < TL::VTHREADS;
-  const int vq = tid / DCH, vch = tid % DCH;
+  // ---- buffer descriptors over this (sequence, group)'s K and V rows; rows >= Tb read as 0
+  const int row_bytes = a.G * D * 2;  // bytes between consecutive tokens
+  const long base_el = ((long)seq0 * a.G + g) * D;
+  const int nrec = (Tb - 1) * row_bytes + D * 2;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(reinterpret_cast<const bf16_t*>(a.kt) + base_el), (short)0, nrec, BUF_RSRC_DW3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(reinterpret_cast<const bf16_t*>(a.v) + base_el), (short)0, nrec, BUF_RSRC_DW3);
 
-  u32x4_t kreg[TL::KPASS];
+  // K tile: DMA straight into LDS. DMA instruction n (= i*4 + wave) fills bytes
+  // [n KB, (n+1) KB) of the tile; lane slot pos of row r receives logical chunk pos ^ (r % DCH),
+  // i.e. the tile is stored XOR-swizzled by 16-byte chunk.
+  int k_voff[KDMA];
+#pragma unroll
+  for (int i = 0; i < KDMA; ++i) {
+    const int n = i * 4 + wave;
+    const int r = n * KROWS_DMA + lane / DCH;
+    const int c = (lane % DCH) ^ (r % DCH);
+    k_voff[i] = r * row_bytes + c * 16;
+  }
+  // V tile: thread (vch = tid / 16, vq = tid % 16) loads keys 4vq..4vq+3 at d-chunk vch.
+  const bool vload = tid < (KT / 4) * DCH;
+  const int vch = tid >> 4, vq = tid & 15;
+  int v_voff[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) v_voff[kk] = (4 * vq + kk) * row_bytes + vch * 16;
+  // V^T destination of this thread: keys 4vq.. -> physical slot 32kb + 16half + 8gg + 4aa
+  int vt_woff[8];
+  {
+    const int kb = vq >> 3, qi = vq & 7;
+    const int half = qi >> 2, aa = (qi >> 1) & 1, gg = qi & 1;
+    const int chunk = 4 * kb + 2 * half + gg;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = 8 * vch + e;
+      vt_woff[e] = KBYTES + d * KT * 2 + ((chunk ^ vt_swz(d)) * 16) + 8 * aa;
+    }
+  }
+  // LDS read offsets (the m-tile and buffer parts are compile-time offsets)
+  int k_roff[NST];
+#pragma unroll
+  for (int st = 0; st < NST; ++st) k_roff[st] = l32 * D * 2 + ((((2 * st + grp) ^ (l32 % DCH))) * 16);
+  int v_roff[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      v_roff[kb][hf] = KBYTES + l32 * KT * 2 + (((4 * kb + 2 * hf + grp) ^ vt_swz(l32)) * 16);
+
   u32x4_t vreg[4];
 
-  auto load_tile = [&](int t) {
-    const int t0 = t * KT;
+  // The buffer index is always a literal at the call sites, so after inlining every LDS
+  // offset below folds into the instructions' immediate offset field.
+  auto issue_tile = [&](int BUF, int t) {
+    const int soff = t * KT * row_bytes;
 #pragma unroll
-    for (int i = 0; i < TL::KPASS; ++i) {
-      const int key = t0 + krow0 + i * TL::KROWS;
-      u32x4_t w = {0u, 0u, 0u, 0u};
-      if (key < Tb) w = *reinterpret_cast<const u32x4_t*>(kg + (long)key * kv_stride + kch * 8);
-      kreg[i] = w;
-    }
+    for (int i = 0; i < KDMA; ++i)
+      dma16(krs, smem + BUF * BUFBYTES + (i * 4 + wave) * 1024, k_voff[i], soff);
     if (vload) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int key = t0 + 4 * vq + kk;
-        u32x4_t w = {0u, 0u, 0u, 0u};
-        if (key < Tb) w = *reinterpret_cast<const u32x4_t*>(vg + (long)key * kv_stride + vch * 8);
-        vreg[kk] = w;
-      }
+      for (int kk = 0; kk < 4; ++kk)
+        vreg[kk] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff[kk], soff, 0));
     }
   };
 
-  auto store_tile = [&](int buf) {
-    bf16_t* ks = smem[buf][0];
-    bf16_t* vs = smem[buf][1];
-#pragma unroll
-    for (int i = 0; i < TL::KPASS; ++i) {
-      const int row = krow0 + i * TL::KROWS;
-      *reinterpret_cast<u32x4_t*>(ks + row * D + ((kch ^ (row & (DCH - 1))) * 8)) = kreg[i];
-    }
+  auto store_vt = [&](int BUF) {
     if (vload) {
-      // keys 4vq..4vq+3 -> physical slot 32kb + 16half + 8grp' + 4a' (see file comment)
-      const int kb = vq >> 3, qi = vq & 7;
-      const int half = qi >> 2, aa = (qi >> 1) & 1, gg = qi & 1;
-      const int chunk = 4 * kb + 2 * half + gg;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        // d = 8 vch + 2w (low halves) and 8 vch + 2w + 1 (high halves)
+        // d = 8 vch + 2w (low halves of the four keys) and d + 1 (high halves)
         const uint32_t lo01 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
         const uint32_t lo23 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x05040100u);
         const uint32_t hi01 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
         const uint32_t hi23 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x07060302u);
-        const int d0 = 8 * vch + 2 * w;
-        const int d1 = d0 + 1;
-        u32x2_t e0 = {lo01, lo23};
-        u32x2_t e1 = {hi01, hi23};
-        *reinterpret_cast<u32x2_t*>(vs + d0 * KT + ((chunk ^ vt_swz(d0)) * 8) + 4 * aa) = e0;
-        *reinterpret_cast<u32x2_t*>(vs + d1 * KT + ((chunk ^ vt_swz(d1)) * 8) + 4 * aa) = e1;
+        *reinterpret_cast<u32x2_t*>(smem + BUF * BUFBYTES + vt_woff[2 * w]) = u32x2_t{lo01, lo23};
+        *reinterpret_cast<u32x2_t*>(smem + BUF * BUFBYTES + vt_woff[2 * w + 1]) = u32x2_t{hi01, hi23};
       }
     }
   };
@@ -186,35 +215,22 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   f32x16_t o[NMT];
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) o[mt] = f32x16_t{};
-  float m_run = -INFINITY;  // running max of this column, in log2 units
+  float m_run = -INFINITY;  // reference max of this column, log2 units
   float l_run = 0.f;        // this lane's share of the running sum
   const float sl2e = a.scale_log2e;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
-    const bool more = t + 1 < ntiles;
-    if (more) load_tile(t + 1);
-
-    const bf16_t* ks = smem[cur][0];
-    const bf16_t* vs = smem[cur][1];
-
+  auto compute_tile = [&](int BUF, int t) {
+    const char* sb = smem + BUF * BUFBYTES;
     // ---- S^T = K Q^T: two 32-key blocks
     f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const int row = 32 * mt + l32;
-        const int ch = 2 * st + grp;
-        const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(ks + row * D + ((ch ^ (row & (DCH - 1))) * 8));
+        const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(sb + k_roff[st] + mt * 32 * D * 2);
         s[mt] = mfma32(as_bf16x8(kw), qf[st], s[mt]);
       }
     }
-
     // ---- mask: only tiles that reach past the wave's lowest position, or past the end
     const int t0 = t * KT;
     if ((a.causal && t0 + KT - 1 > p_wlo) || t0 + KT > Tb) {
@@ -227,14 +243,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
         }
       }
     }
-
-    // ---- online softmax of this column (lanes l and l^32 share it)
-    float mx = -INFINITY;
+    // ---- online softmax of this column (lanes l and l^32 share it), lazy rescale
+    float mx = fmaxf(s[0][0], s[1][0]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(s[0][i], s[1][i]));
-    mx = fmaxf(mx, xor_shfl(mx, 32));
-    const float m_new = fmaxf(m_run, mx * sl2e);
-    if (__any(m_new > m_run)) {
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s[0][i], s[1][i]));
+    mx = fmaxf(mx, xor_shfl(mx, 32)) * sl2e;
+    if (__any(mx > m_run + TAU)) {
+      const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
@@ -257,25 +272,40 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
         pb[kb][hf] = as_bf16x8(w);
       }
     }
-
     // ---- O^T += V^T P^T
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
-      const int d = 32 * mt + l32;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const int ch = 4 * kb + 2 * hf + grp;
-          const u32x4_t vw = *reinterpret_cast<const u32x4_t*>(vs + d * KT + ((ch ^ vt_swz(d)) * 8));
+          const u32x4_t vw = *reinterpret_cast<const u32x4_t*>(sb + v_roff[kb][hf] + mt * 32 * KT * 2);
           o[mt] = mfma32(as_bf16x8(vw), pb[kb][hf], o[mt]);
         }
       }
     }
+  };
 
-    if (more) store_tile(cur ^ 1);
+  // ---- pipeline: tile t+1 is in flight (K by DMA, V in registers) while tile t computes
+  auto step = [&](int cur, int nxt, int t) {
+    const bool more = t + 1 < ntiles;
+    if (more) issue_tile(nxt, t + 1);
+    compute_tile(cur, t);
+    if (more) store_vt(nxt);
+    wait_vmem();
     __syncthreads();
+  };
+
+  issue_tile(0, 0);
+  store_vt(0);
+  wait_vmem();
+  __syncthreads();
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    step(0, 1, t);
+    step(1, 0, t + 1);
   }
+  if (t < ntiles) step(0, 1, t);
 
   // ---- epilogue: O / l -> bf16
   const float l_tot = l_run + xor_shfl(l_run, 32);
