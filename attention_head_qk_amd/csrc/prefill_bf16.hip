@@ -18,15 +18,19 @@
 //   of a column lives in one lane (plus its partner lane l^32 for the other half of the
 //   keys), and the bf16-packed probabilities already sit in the B-operand layout of the
 //   second product O^T = V^T P^T: no LDS round trip for P.
-// * V^T in LDS. The A operand of O^T needs 8 consecutive keys per lane, so V tiles are
-//   transposed on their way into LDS (4 keys x 8 d per thread, v_perm_b32 regroups the
-//   halves, 8-byte LDS stores), with the key order inside each 16-key step permuted so the
-//   8 keys a lane needs are one 16-byte LDS read. K and V^T rows are XOR-swizzled in 16-byte
-//   chunks to spread LDS banks.
-// * Pipeline. LDS is double-buffered: the global loads of tile t+1 are issued before the
-//   MFMAs of tile t and written to the other buffer after them; one barrier per tile.
-// * Softmax in base 2 with scale*log2(e) folded into one FMA per score; the O rescale is
-//   skipped when no column's max moved (a wave-uniform test).
+// * K tiles go global -> LDS by DMA (16-byte buffer loads into LDS), XOR-swizzled by 16-byte
+//   chunk. The A operand of O^T needs 8 consecutive keys per lane, so V tiles are loaded
+//   into registers and transposed on their way into LDS (4 keys x 8 d per thread, v_perm_b32
+//   regroups the halves, 8-byte stores), with the key order inside each 16-key step permuted
+//   so the 8 keys a lane needs are one 16-byte read. Both layouts are bank-conflict free for
+//   the reads and writes they see. Buffer descriptors bound each sequence, so rows past its
+//   end read as zero without per-load tests, and every LDS address is computed once.
+// * Pipeline. LDS is double-buffered: the loads of tile t+1 are issued before the MFMAs of
+//   tile t and the V^T store follows them; one barrier per tile.
+// * Softmax in base 2 with scale*log2(e) folded into one FMA per score. The reference max
+//   of a column only moves when the probabilities it gives would exceed 2^32 (a wave-uniform
+//   test on the tile sums), so the common tile needs neither a max nor an O rescale; the
+//   result is unchanged because softmax does not depend on the subtracted constant.
 // * Scheduling. Blocks are issued heaviest first (descending position) so the causal
 //   triangle drains without a long tail, and the group index is the fastest-varying part of
 //   the block id, which keeps the blocks of one KV group on the same XCD (blocks are dealt
@@ -40,7 +44,6 @@ namespace {
 
 constexpr int KT = 64;      // keys per tile
 constexpr int COLS = 128;   // columns per workgroup (4 waves x 32)
-constexpr float TAU = 8.0f; // lazy-rescale threshold, log2 units: probabilities stay <= 2^8
 constexpr int BUF_RSRC_DW3 = 0x00020000;  // buffer descriptor word 3 for gfx9-class parts
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t w) { return __builtin_bit_cast(bf16x8_t, w); }
@@ -84,7 +87,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep it scalar
   const int l32 = lane & 31;
   const int grp = lane >> 5;
 
@@ -231,47 +234,62 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
         s[mt] = mfma32(as_bf16x8(kw), qf[st], s[mt]);
       }
     }
-    // ---- mask: only tiles that reach past the wave's lowest position, or past the end
+    // ---- mask: only tiles that reach past the wave's lowest position, or past the end.
+    // key = t0 + 32 mt + 8 (i/4) + 4 grp + i%4 is visible iff key <= min(plim, Tb - 1).
     const int t0 = t * KT;
     if ((a.causal && t0 + KT - 1 > p_wlo) || t0 + KT > Tb) {
+      const int lim = (plim < Tb - 1 ? plim : Tb - 1) - t0 - 4 * grp;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = t0 + 32 * mt + 8 * (i >> 2) + 4 * grp + (i & 3);
-          if (key > plim || key >= Tb) s[mt][i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i)
+          if (32 * mt + 8 * (i >> 2) + (i & 3) > lim) s[mt][i] = -INFINITY;
       }
     }
-    // ---- online softmax of this column (lanes l and l^32 share it), lazy rescale
-    float mx = fmaxf(s[0][0], s[1][0]);
+    // ---- probabilities against the column's reference max m_run (log2 units). The common
+    // case needs no max at all: P = 2^(s*c - m_run) is accepted while every lane's tile sum
+    // stays <= 2^32 (so every P does); otherwise (always on the first tile, where m_run is
+    // -inf) the wave takes the exact path: tile max, new reference, rescale O and l, redo P.
+    // The row sum is taken over the bf16-rounded P that also feeds the P.V product.
+    const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+    uint32_t pk[2][8];
+    float ls = 0.f;
+    auto probs = [&]() {
+      ls = 0.f;
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s[0][i], s[1][i]));
-    mx = fmaxf(mx, xor_shfl(mx, 32)) * sl2e;
-    if (__any(mx > m_run + TAU)) {
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * j], sl2e, -m_run));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * j + 1], sl2e, -m_run));
+          f32x2_t pp = {p0, p1};
+          const bf16x2_t pb2 = __builtin_convertvector(pp, bf16x2_t);
+          pk[kb][j] = __builtin_bit_cast(uint32_t, pb2);
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pb2, one2, ls, false);
+        }
+      }
+    };
+    probs();
+    if (__any(!(ls <= 0x1p32f))) {
+      float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s[0][i], s[1][i]));
+      mx = fmaxf(mx, xor_shfl(mx, 32)) * sl2e;
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt) o[mt] *= alpha;
       m_run = m_new;
+      probs();
     }
+    l_run += ls;
     bf16x8_t pb[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        float p[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          p[j] = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hf + j], sl2e, -m_run));
-          l_run += p[j];
-        }
-        u32x4_t w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                     pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-        pb[kb][hf] = as_bf16x8(w);
-      }
-    }
+      for (int hf = 0; hf < 2; ++hf)
+        pb[kb][hf] = as_bf16x8(u32x4_t{pk[kb][4 * hf], pk[kb][4 * hf + 1], pk[kb][4 * hf + 2], pk[kb][4 * hf + 3]});
     // ---- O^T += V^T P^T
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
