@@ -208,24 +208,284 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------- bf16: matrix cores
+//
+// bf16 split pass on v_mfma_f32_16x16x32_bf16. Per wave, 32 keys at a time:
+//   S^T = K Q^T   A = K rows straight from global (lane: key l%16, 8 consecutive d), B = the
+//                 group's query heads (one head per column, padded to 16 columns);
+//   O^T += V^T P^T  A = V^T, read from the V rows staged in LDS (16-byte DMA) with
+//                 ds_read_b64_tr_b16, which hands each lane 4 consecutive keys of one d;
+//                 B = P^T, which is the S^T accumulator itself, exponentiated and packed.
+// In the 16x16 accumulator lane l owns head l%16, so a head's online softmax lives in the 4
+// lanes l%16 + 16q. The reference max only moves when a probability would exceed 2^32 (the
+// same lazy rule as the prefill kernel). Each of the 4 waves covers a quarter of the split
+// with its own state; the states merge through LDS at the end.
+namespace {
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ds_read_b64_tr_b16: inside every 16-lane block, lane i receives element i%4 of the 8-byte
+// values addressed by lanes 4j + i/4 of that block, j = 0..3.
+__device__ __forceinline__ u32x2_t ds_read_tr16(const char* lds) {
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)lds);
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+// XOR swizzle of the 16-byte chunk index of a staged V row: the four rows one transposing
+// read touches land on four different chunk pairs, so the read is bank-conflict free.
+__device__ __forceinline__ int v_swz(int row) { return 2 * (row & 3); }
+
+}  // namespace
+
+template <int D, int HT>
+__global__ __launch_bounds__(256, 2) void decode_split_mfma_kernel(DecodeArgs a) {
+  constexpr int KSTEP = D / 32;             // k-steps of S^T
+  constexpr int NMT = D / 16;               // 16-row tiles of O^T
+  constexpr int SUB = 32;                   // keys per step of a wave
+  constexpr int KPW = kDecodeSplit / 4;     // keys per wave
+  constexpr int ROWB = D * 2;               // bytes of one staged V row
+  constexpr int SUBB = SUB * ROWB;          // one staged V sub-tile
+  constexpr int NDMA = SUBB / 1024;         // 1 KB DMA instructions per sub-tile
+  constexpr int DCH = D / 8;                // 16-byte chunks per row
+  constexpr int NHEAD = 16 * HT;
+  constexpr int MERGEB = 4 * NHEAD * (D + 2) * 4;
+  constexpr int SMEMB = (4 * SUBB > MERGEB) ? 4 * SUBB : MERGEB;
+  __shared__ __attribute__((aligned(16))) char smem[SMEMB];
+
+  const int s = blockIdx.x;
+  const int b = blockIdx.z;
+  const int nht = (a.h + NHEAD - 1) / NHEAD;
+  const int g = blockIdx.y / nht;
+  const int head0 = (blockIdx.y % nht) * NHEAD;  // first head (inside the group) of this block
+  const int L = a.seq_lens[b];
+  const int k0 = s * kDecodeSplit;
+  if (k0 >= L) return;
+  const int k1 = (k0 + kDecodeSplit < L) ? k0 + kDecodeSplit : L;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, q4 = lane >> 4;
+  const int h = a.h;
+  const float sl2e = a.scale_log2e;
+
+  // ---- Q^T (B operand): column = head head0 + 16 ht + l16, d = 32 st + 8 q4 + [0, 8)
+  bf16x8_t qf[HT][KSTEP];
+  {
+    const bf16_t* qt = reinterpret_cast<const bf16_t*>(a.qt) + ((long)b * a.H + (long)g * h) * D;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int hh = head0 + 16 * ht + l16;
+#pragma unroll
+      for (int st = 0; st < KSTEP; ++st) {
+        u32x4_t w = {0u, 0u, 0u, 0u};
+        if (hh < h) w = *reinterpret_cast<const u32x4_t*>(qt + (long)hh * D + 32 * st + 8 * q4);
+        qf[ht][st] = as_bf16x8(w);
+      }
+    }
+  }
+
+  // ---- buffer descriptors over sequence b's rows of group g; rows >= L read as zero
+  const int row_stride = a.G * D * 2;
+  const long base_el = ((long)b * a.max_seq * a.G + g) * D;
+  const int nrec = (L - 1) * row_stride + D * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(reinterpret_cast<const bf16_t*>(a.k_cache) + base_el, nrec);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(reinterpret_cast<const bf16_t*>(a.v_cache) + base_el, nrec);
+
+  f32x4_t o[HT][NMT];
+  float m_run[HT], l_run[HT];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    m_run[ht] = -INFINITY;
+    l_run[ht] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) o[ht][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  char* vbuf = smem + wave * SUBB;
+  const int kw0 = k0 + wave * KPW;
+  const int kw1 = (kw0 + KPW < k1) ? kw0 + KPW : k1;
+  const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+
+  for (int kb = kw0; kb < kw1; kb += SUB) {
+    // V rows kb..kb+31 -> LDS. DMA instruction n fills rows n*RPD .. (RPD = rows per KB); lane
+    // slot pos of row r receives logical chunk pos ^ v_swz(r).
+#pragma unroll
+    for (int n = 0; n < NDMA; ++n) {
+      const int r = n * (1024 / ROWB) + lane / DCH;
+      const int c = (lane % DCH) ^ v_swz(r);
+      dma16(vrs, vbuf + n * 1024, (kb + r) * row_stride + c * 16, 0);
+    }
+    // K rows as A operands: tile tt holds keys kb + 16 tt + l16, d = 32 st + 8 q4 + [0, 8)
+    u32x4_t kr[2][KSTEP];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int st = 0; st < KSTEP; ++st)
+        kr[tt][st] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+            krs, (kb + 16 * tt + l16) * row_stride + (32 * st + 8 * q4) * 2, 0, 0));
+    // ---- S^T: keys (kb + 16 tt + 4 q4 + i) x heads
+    f32x4_t sc[2][HT];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < KSTEP; ++st) acc = mfma16(as_bf16x8(kr[tt][st]), qf[ht][st], acc);
+        sc[tt][ht] = acc;
+      }
+    if (kb + SUB > kw1) {  // the last step of the sequence: keys >= kw1 are not there
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (kb + 16 * tt + 4 * q4 + i >= kw1)
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) sc[tt][ht][i] = -INFINITY;
+    }
+    // ---- probabilities (P^T as the B operand: slots 0-3 from tile 0, 4-7 from tile 1)
+    bf16x8_t pb[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      uint32_t pk[4];
+      float ls;
+      auto probs = [&]() {
+        ls = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            f32x2_t pp = {__builtin_amdgcn_exp2f(fmaf(sc[tt][ht][2 * j], sl2e, -m_run[ht])),
+                          __builtin_amdgcn_exp2f(fmaf(sc[tt][ht][2 * j + 1], sl2e, -m_run[ht]))};
+            const bf16x2_t pb2 = __builtin_convertvector(pp, bf16x2_t);
+            pk[2 * tt + j] = __builtin_bit_cast(uint32_t, pb2);
+            ls = __builtin_amdgcn_fdot2_f32_bf16(pb2, one2, ls, false);
+          }
+      };
+      probs();
+      if (__any(!(ls <= 0x1p32f))) {
+        float mx = fmaxf(fmaxf(sc[0][ht][0], sc[0][ht][1]), fmaxf(sc[0][ht][2], sc[0][ht][3]));
+        mx = fmaxf(mx, fmaxf(fmaxf(sc[1][ht][0], sc[1][ht][1]), fmaxf(sc[1][ht][2], sc[1][ht][3])));
+        mx = fmaxf(mx, xor_shfl(mx, 16));
+        mx = fmaxf(mx, xor_shfl(mx, 32)) * sl2e;
+        const float m_new = fmaxf(m_run[ht], mx);
+        if (m_new != -INFINITY) {  // padded or fully masked heads keep their state
+          const float alpha = __builtin_amdgcn_exp2f(m_run[ht] - m_new);
+          l_run[ht] *= alpha;
+#pragma unroll
+          for (int mt = 0; mt < NMT; ++mt) o[ht][mt] *= alpha;
+          m_run[ht] = m_new;
+        }
+        probs();
+      }
+      l_run[ht] += ls;
+      pb[ht] = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+    }
+    // ---- O^T += V^T P^T; V^T operand: lane (d = 16 mt + l16) gets keys 4 q4 + 0..3 from the
+    // first transposing read and 16 + 4 q4 + 0..3 from the second
+    wait_vmem();
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const int r0 = 4 * q4 + (l16 >> 2);
+      const int c = 2 * mt + ((l16 & 3) >> 1);
+      const int off8 = (l16 & 1) * 8;
+      const u32x2_t v0 = ds_read_tr16(vbuf + r0 * ROWB + ((c ^ v_swz(r0)) * 16) + off8);
+      const u32x2_t v1 = ds_read_tr16(vbuf + (r0 + 16) * ROWB + ((c ^ v_swz(r0 + 16)) * 16) + off8);
+      const bf16x8_t va = as_bf16x8(u32x4_t{v0[0], v0[1], v1[0], v1[1]});
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) o[ht][mt] = mfma16(va, pb[ht], o[ht][mt]);
+    }
+  }
+
+  // ---- merge the 4 waves' states; layout sm_m[w][head], sm_l[w][head], sm_o[w][head][d]
+  __syncthreads();  // staged V no longer needed: reuse LDS
+  float* sm_m = reinterpret_cast<float*>(smem);
+  float* sm_l = sm_m + 4 * NHEAD;
+  float* sm_o = sm_l + 4 * NHEAD;
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    float lt = l_run[ht] + xor_shfl(l_run[ht], 16);
+    lt += xor_shfl(lt, 32);
+    const int hh = 16 * ht + l16;
+    if (q4 == 0) {
+      sm_m[wave * NHEAD + hh] = m_run[ht];
+      sm_l[wave * NHEAD + hh] = lt;
+    }
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm_o[(wave * NHEAD + hh) * D + 16 * mt + 4 * q4 + i] = o[ht][mt][i];
+  }
+  __syncthreads();
+  const int nh = (h - head0 < NHEAD) ? h - head0 : NHEAD;
+  for (int idx = tid; idx < nh * D; idx += 256) {
+    const int hh = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w * NHEAD + hh]);
+    float Ls = 0.f, Os = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float wt = __builtin_amdgcn_exp2f(sm_m[w * NHEAD + hh] - M);  // empty waves: 0
+      Ls = fmaf(sm_l[w * NHEAD + hh], wt, Ls);
+      Os = fmaf(sm_o[(w * NHEAD + hh) * D + d], wt, Os);
+    }
+    const long pidx = ((long)b * a.H + (long)g * h + head0 + hh) * a.nsplit + s;
+    a.part_o[pidx * D + d] = Os;
+    if (d == 0) {
+      a.part_ml[2 * pidx] = M;
+      a.part_ml[2 * pidx + 1] = Ls;
+    }
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
+  __shared__ float sw[kMaxCombineSplits];
+  __shared__ float s_inv;
   const int head = blockIdx.x;
   const int b = blockIdx.y;
   const int d = threadIdx.x;
   const int L = a.seq_lens[b];
   const int ns = (L + kDecodeSplit - 1) / kDecodeSplit;
   const long base = ((long)b * a.H + head) * a.nsplit;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[2 * (base + s)]);
-  float Ls = 0.f, Os = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = __builtin_amdgcn_exp2f(a.part_ml[2 * (base + s)] - M);
-    Ls = fmaf(a.part_ml[2 * (base + s) + 1], w, Ls);
-    Os = fmaf(a.part_o[(base + s) * D + d], w, Os);
-  }
-  const float r = (ns > 0) ? Os / Ls : 0.f;
   T* out = reinterpret_cast<T*>(a.out) + ((long)b * a.H + head) * D + d;
+  if (ns == 0) {
+    if constexpr (sizeof(T) == 2) *out = (bf16_t)0;
+    else *out = 0.f;
+    return;
+  }
+  // the first wave turns the split maxima into weights 2^(m_s - M) and the total 1 / L
+  if (d < 64) {
+    float M = -INFINITY;
+    for (int s = d; s < ns; s += 64) M = fmaxf(M, a.part_ml[2 * (base + s)]);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, xor_shfl(M, m));
+    float Ls = 0.f;
+    for (int s = d; s < ns; s += 64) {
+      const float w = __builtin_amdgcn_exp2f(a.part_ml[2 * (base + s)] - M);
+      sw[s] = w;
+      Ls = fmaf(a.part_ml[2 * (base + s) + 1], w, Ls);
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) Ls += xor_shfl(Ls, m);
+    if (d == 0) s_inv = 1.0f / Ls;
+  }
+  __syncthreads();
+  const float* po = a.part_o + base * D + d;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + 4 <= ns; s += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] = fmaf(po[(long)(s + u) * D], sw[s + u], acc[u]);
+  }
+  for (; s < ns; ++s) acc[0] = fmaf(po[(long)s * D], sw[s], acc[0]);
+  const float r = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * s_inv;
   if constexpr (sizeof(T) == 2) {
     *out = (bf16_t)(pack_bf16x2(r, 0.f) & 0xffffu);
   } else {
@@ -253,9 +513,22 @@ static hipError_t combine_td(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, int HT>
+static hipError_t launch_split_mfma(const DecodeArgs& a, hipStream_t s) {
+  const int nht = (a.h + 16 * HT - 1) / (16 * HT);
+  const dim3 grid(a.nsplit, a.G * nht, a.B);
+  hipLaunchKernelGGL((decode_split_mfma_kernel<D, HT>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t split_mfma_d(const DecodeArgs& a, hipStream_t s) {
+  return a.h <= 16 ? launch_split_mfma<D, 1>(a, s) : launch_split_mfma<D, 2>(a, s);
+}
+
 hipError_t launch_decode_split(const DecodeArgs& a, int d, bool bf16, hipStream_t s) {
   if (a.B <= 0) return hipSuccess;
-  if (bf16) return d == 128 ? split_td<bf16_t, 128>(a, s) : split_td<bf16_t, 64>(a, s);
+  if (bf16) return d == 128 ? split_mfma_d<128>(a, s) : split_mfma_d<64>(a, s);
   return d == 128 ? split_td<float, 128>(a, s) : split_td<float, 64>(a, s);
 }
 

@@ -80,6 +80,26 @@ __device__ __forceinline__ void store8(bf16_t* p, const float x[8]) {
 
 __device__ __forceinline__ float xor_shfl(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t w) { return __builtin_bit_cast(bf16x8_t, w); }
+
+constexpr int BUF_RSRC_DW3 = 0x00020000;  // buffer descriptor word 3 for gfx9-class parts
+
+// Buffer descriptor over [base, base + nbytes): loads past the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, BUF_RSRC_DW3);
+}
+
+// Wait for every outstanding vector-memory load of this wave, including LDS DMA
+// (s_waitcnt vmcnt(0); gfx9 encoding: expcnt and lgkmcnt fields left at their maxima).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// 16 bytes per lane from a buffer straight into LDS: lane i lands at lds + 16 i (the LDS
+// address is taken from the first lane, so it must be the same for the whole wave).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, const char* lds, int voff, int soff) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)lds, 16, voff, soff, 0, 0);
+}
+
 // Sum over aligned groups of W consecutive lanes (W a power of two <= 64).
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
@@ -118,6 +138,7 @@ struct PrefillArgs {
   int B, T, H, G, h;
   int causal;
   int n_blk;          // column blocks of the longest sequence
+  int zigzag;         // 1: pair heavy and light blocks (see the prefill kernel)
   float scale;        // score scale (1/sqrt(d) by default)
   float scale_log2e;  // scale * log2(e)
 };
@@ -134,6 +155,7 @@ struct DecodeArgs {
   float scale_log2e;
 };
 
-constexpr int kDecodeSplit = 512;  // keys per split of the decode pass
+constexpr int kDecodeSplit = 512;        // keys per split of the decode pass
+constexpr int kMaxCombineSplits = 4096;  // splits per sequence the combine pass can merge
 
 }  // namespace gqa

@@ -174,6 +174,16 @@ gqa_status gqa_prefill(const void* q, const void* k, const void* v, const int32_
   const long cols = (long)T * fa.h;
   const int cpb = gqa::prefill_bf16_cols_per_block();
   fa.n_blk = (int)((cols + cpb - 1) / cpb);
+  // Pair heavy and light causal blocks when the grid is at most about two workgroups per CU
+  // (two bf16 prefill workgroups are resident per CU); longer grids run heaviest first.
+  {
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return GQA_EHIP;
+    const long grid = (long)B * G * fa.n_blk;
+    fa.zigzag = (causal && !p->cu_seqlens && grid <= 4L * n_cu) ? 1 : 0;
+  }
   fa.scale = eff_scale(p, d);
   fa.scale_log2e = (float)((double)fa.scale * 1.4426950408889634074);
   if ((st = from_hip(mark(p->prof_start, stream))) != GQA_OK) return st;
@@ -192,6 +202,11 @@ gqa_status gqa_decode(const void* q, void* k_cache, void* v_cache, const int32_t
   if (B < 0 || max_seq < 0) return GQA_EINVAL;
   if (B == 0) return GQA_OK;
   if (max_seq == 0) return GQA_EINVAL;
+  // one sequence's cache rows are addressed with 32-bit byte offsets, and the combine pass
+  // merges at most kMaxCombineSplits splits per sequence
+  if ((long long)max_seq * G * d * (long long)elem_size(p->dtype) > 0x7fffffffLL ||
+      decode_nsplit(max_seq) > gqa::kMaxCombineSplits)
+    return GQA_ENOTSUP;
   if (!tensor_ok(q) || !tensor_ok(k_cache) || !tensor_ok(v_cache) || !tensor_ok(out))
     return GQA_EINVAL;
   if (!seq_lens || !opt_int_ok(seq_lens) || !opt_int_ok(p->positions)) return GQA_EINVAL;

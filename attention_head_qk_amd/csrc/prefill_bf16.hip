@@ -32,9 +32,11 @@
 //   test on the tile sums), so the common tile needs neither a max nor an O rescale; the
 //   result is unchanged because softmax does not depend on the subtracted constant.
 // * Scheduling. Blocks are issued heaviest first (descending position) so the causal
-//   triangle drains without a long tail, and the group index is the fastest-varying part of
-//   the block id, which keeps the blocks of one KV group on the same XCD (blocks are dealt
-//   round-robin over the 8 XCDs) when G is a multiple of 8, so its K/V stay in that L2.
+//   triangle drains without a long tail; when the whole grid fits on the chip in about two
+//   rounds, heavy and light blocks are paired instead (zigzag). The group index is the
+//   fastest-varying part of the block id, which keeps the blocks of one KV group on the same
+//   XCD (blocks are dealt round-robin over the 8 XCDs) when G is a multiple of 8, so its K/V
+//   stay in that XCD's L2.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -44,23 +46,6 @@ namespace {
 
 constexpr int KT = 64;      // keys per tile
 constexpr int COLS = 128;   // columns per workgroup (4 waves x 32)
-constexpr int BUF_RSRC_DW3 = 0x00020000;  // buffer descriptor word 3 for gfx9-class parts
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t w) { return __builtin_bit_cast(bf16x8_t, w); }
-
-// Wait for every outstanding vector-memory load of this wave, including LDS DMA
-// (s_waitcnt vmcnt(0); gfx9 encoding: expcnt and lgkmcnt fields left at their maxima).
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// 16 bytes per lane from a buffer straight into LDS: lane i lands at lds + 16 i.
-// The builtin exists only for the device; clang's host pass drops the kernel's launch stub
-// when it sees it, so the host pass gets an empty body (it never runs device code anyway).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, const char* lds, int voff, int soff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  typedef __attribute__((address_space(3))) void lds_void;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)lds, 16, voff, soff, 0, 0);
-#endif
-}
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -91,12 +76,17 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   const int l32 = lane & 31;
   const int grp = lane >> 5;
 
-  // ---- block -> (sequence, group, column block), heaviest first
+  // ---- block -> (sequence, group, column block). Heaviest first; with zigzag the second
+  // half of the grid runs lightest first instead, so that block ids i and i + grid/2, which
+  // the dispatcher places on the same CU when the whole grid is resident at once, carry
+  // complementary causal work (n_blk - r and r + 1 tiles).
   const int id = blockIdx.x;
   const int g = id % a.G;
   const int rest = id / a.G;
   const int b = rest % a.B;
-  const int blk = a.n_blk - 1 - rest / a.B;
+  const int r = rest / a.B;
+  const int half_r = (a.n_blk + 1) / 2;
+  const int blk = (a.zigzag && r >= half_r) ? r - half_r : a.n_blk - 1 - r;
   int seq0, Tb;
   if (a.cu_seqlens) {
     seq0 = a.cu_seqlens[b];
@@ -139,10 +129,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   const int row_bytes = a.G * D * 2;  // bytes between consecutive tokens
   const long base_el = ((long)seq0 * a.G + g) * D;
   const int nrec = (Tb - 1) * row_bytes + D * 2;
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(reinterpret_cast<const bf16_t*>(a.kt) + base_el), (short)0, nrec, BUF_RSRC_DW3);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(reinterpret_cast<const bf16_t*>(a.v) + base_el), (short)0, nrec, BUF_RSRC_DW3);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(reinterpret_cast<const bf16_t*>(a.kt) + base_el, nrec);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(reinterpret_cast<const bf16_t*>(a.v) + base_el, nrec);
 
   // K tile: DMA straight into LDS. DMA instruction n (= i*4 + wave) fills bytes
   // [n KB, (n+1) KB) of the tile; lane slot pos of row r receives logical chunk pos ^ (r % DCH),

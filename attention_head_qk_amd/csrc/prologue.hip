@@ -6,163 +6,154 @@
 // adjacent pair (2j, 2j+1) counter-clockwise by pos * omega_j (D2-2 matrix R(pos); ewbang.com
 // "深入剖析Qwen3模型架构" 3.1.2 and 3.4.1 for the pairing and omega_j = theta^(-2j/d)).
 //
-// One workgroup per token (prefill) or per sequence (decode). The angles of a token are the
-// same for all its H + G heads, so one wave evaluates cos/sin of the d/2 angles once, in
-// fp64 after an exact-ish fp64 range reduction, and parks them in LDS; then every wave
-// streams head rows: 8 elements per lane (one 16-byte load for bf16), d/8 lanes per row,
-// the sum of squares reduced across those lanes with shuffles. The kernel is HBM-bound
-// (reads and writes (H+G)*d elements per token).
+// HBM-bound: it reads and writes (H + G) * d elements per token. Every lane owns one 16-byte
+// chunk (4 rotation pairs) of one head row of one token, so the whole tensor is in flight at
+// once; d/8 lanes cover a row with one coalesced read, the sum of squares is reduced across
+// them with DPP row permutes, and each lane evaluates its own four angles (cheap next to the
+// row's HBM traffic). Angles: pos * omega_j and its reduction to revolutions
+// are done in fp64 (exact to ~1e-12 rad at pos 32767); bf16 outputs then take the hardware
+// sin/cos of the fp32 revolution count (abs error ~1e-6, far below bf16 rounding), fp32
+// outputs an fp64 sincos.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace gqa {
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void qk_norm_rope_kernel(PrologueArgs a) {
-  constexpr int LPR = D / 8;        // lanes per head row
-  constexpr int RPW = 64 / LPR;     // rows per wave pass
-  constexpr int RPB = 4 * RPW;      // rows per workgroup pass
-  __shared__ float cs[D / 2];
-  __shared__ float sn[D / 2];
+namespace {
 
-  const int tid = threadIdx.x;
-  long row_in;    // index of the q row block [H, D] of this token / sequence
-  long k_row_out; // destination row block of K (and V) in k_out / v_out; -1 = no K output
-  int pos;
-  if (!a.decode) {
-    int b, t, Tb;
-    if (a.cu_seqlens) {
-      b = blockIdx.x / a.T;
-      t = blockIdx.x % a.T;
-      const int s0 = a.cu_seqlens[b];
-      Tb = a.cu_seqlens[b + 1] - s0;
-      if (t >= Tb) return;
-      row_in = s0 + t;
-    } else {
-      b = blockIdx.x / a.T;
-      t = blockIdx.x % a.T;
-      row_in = blockIdx.x;
-    }
-    pos = a.positions ? a.positions[row_in] : t;
-    k_row_out = a.k ? row_in : -1;
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int x = __builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true);
+  return v + __int_as_float(x);
+}
+
+// Sum over aligned groups of W lanes (W = 8 or 16) inside a DPP row.
+template <int W>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  v = dpp_add<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_add<0x141>(v);  // row_half_mirror
+  if (W == 16) v = dpp_add<0x140>(v);  // row_mirror
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ void rope_cs(double phi, float& c, float& s) {
+  // revolutions in [0, 1), reduced in fp64
+  const double rev = phi * 0.15915494309189533577;  // 1 / (2 pi)
+  const float r = (float)(rev - floor(rev));
+  if constexpr (sizeof(T) == 2) {
+    s = __builtin_amdgcn_sinf(r);  // sin(2 pi r)
+    c = __builtin_amdgcn_cosf(r);
   } else {
-    const int b = blockIdx.x;
-    const int L = a.seq_lens[b];
-    pos = a.positions ? a.positions[b] : (L > 0 ? L - 1 : 0);
-    row_in = b;
-    k_row_out = (a.k && L > 0) ? ((long)b * a.max_seq + (L - 1)) : -1;
-  }
-
-  if (a.use_rope) {
-    if (tid < D / 2) {
-      // fp64 angle, reduced to [-pi, pi] before the fp64 sincos.
-      const double phi = (double)pos * a.omega[tid];
-      const double two_pi = 6.283185307179586476925286766559;
-      const double r = phi - rint(phi / two_pi) * two_pi;
-      double s, c;
-      sincos(r, &s, &c);
-      cs[tid] = (float)c;
-      sn[tid] = (float)s;
-    }
-    __syncthreads();
-  }
-
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int sub = lane / LPR;       // row slot within the wave pass
-  const int ch = lane % LPR;        // 8-element chunk of the row
-  const int e0 = ch * 8;
-
-  float gq[8], gk[8];
-  const bool norm_q = a.gq != nullptr, norm_k = a.gk != nullptr;
-  if (norm_q) load8(reinterpret_cast<const T*>(a.gq) + e0, gq);
-  if (norm_k) load8(reinterpret_cast<const T*>(a.gk) + e0, gk);
-  float c4[4], s4[4];
-  if (a.use_rope) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      c4[m] = cs[ch * 4 + m];
-      s4[m] = sn[ch * 4 + m];
-    }
-  }
-
-  const int nq = a.H;
-  const int nk = (k_row_out >= 0) ? a.G : 0;
-  const int nv = (a.decode && a.v && k_row_out >= 0) ? a.G : 0;
-  const int total = nq + nk + nv;
-  const T* qin = reinterpret_cast<const T*>(a.q) + row_in * (long)a.H * D;
-  T* qout = reinterpret_cast<T*>(a.q_out) + row_in * (long)a.H * D;
-
-  for (int r0 = 0; r0 < total; r0 += RPB) {
-    const int r = r0 + wave * RPW + sub;
-    const bool active = r < total;
-    float x[8];
-    const T* src;
-    T* dst;
-    bool norm, rope_it;
-    const float* gam;
-    if (r < nq) {
-      src = qin + (long)r * D;
-      dst = qout + (long)r * D;
-      norm = norm_q;
-      gam = gq;
-      rope_it = true;
-    } else if (r < nq + nk) {
-      const int g = r - nq;
-      src = reinterpret_cast<const T*>(a.k) + (row_in * (long)a.G + g) * D;
-      dst = reinterpret_cast<T*>(a.k_out) + (k_row_out * a.G + g) * D;
-      norm = norm_k;
-      gam = gk;
-      rope_it = true;
-    } else {
-      const int g = r - nq - nk;
-      src = reinterpret_cast<const T*>(a.v) + (row_in * (long)a.G + g) * D;
-      dst = reinterpret_cast<T*>(a.v_out) + (k_row_out * a.G + g) * D;
-      norm = false;
-      gam = gq;
-      rope_it = false;
-    }
-    if (active) {
-      load8(src + e0, x);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = 0.f;
-    }
-    // Row type is uniform across the LPR lanes of a row, so the reduction below only mixes
-    // lanes that agree on `norm`.
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
-    ss = group_sum<LPR>(ss);
-    if (norm) {
-      const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = (x[i] * rinv) * gam[i];
-    }
-    if (rope_it && a.use_rope) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float x0 = x[2 * m], x1 = x[2 * m + 1];
-        x[2 * m] = x0 * c4[m] - x1 * s4[m];
-        x[2 * m + 1] = x0 * s4[m] + x1 * c4[m];
-      }
-    }
-    if (active) store8(dst + e0, x);
+    double sd, cd;
+    sincos(phi - floor(rev) * 6.283185307179586476925286766559, &sd, &cd);
+    s = (float)sd;
+    c = (float)cd;
   }
 }
 
+}  // namespace
+
 template <typename T, int D>
-static hipError_t launch_prologue_t(const PrologueArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((qk_norm_rope_kernel<T, D>), dim3(grid), dim3(256), 0, s, a);
+__global__ __launch_bounds__(256) void qk_norm_rope_kernel(PrologueArgs a) {
+  constexpr int LPR = D / 8;  // lanes per head row (8 elements = one 16-byte bf16 chunk each)
+  const int rows_per_token = a.H + (a.k ? a.G : 0) + ((a.decode && a.v) ? a.G : 0);
+  const long item = (long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;  // (token slot, row)
+  const int ch = threadIdx.x % LPR;
+  const int e0 = ch * 8;
+  const int slot = (int)(item / rows_per_token);
+  const int r = (int)(item % rows_per_token);
+
+  // ---- the token this row belongs to, its RoPE position, and the row's source/destination
+  bool active;
+  long tok = 0;        // token index of the source rows
+  long k_tok_out = 0;  // destination token row for K / V
+  int pos = 0;
+  if (!a.decode) {
+    const int b = slot / a.T, t = slot % a.T;
+    active = b < a.B;
+    if (active && a.cu_seqlens) {
+      const int s0 = a.cu_seqlens[b];
+      active = t < a.cu_seqlens[b + 1] - s0;
+      tok = s0 + t;
+    } else {
+      tok = slot;
+    }
+    if (active) pos = a.positions ? a.positions[tok] : t;
+    k_tok_out = tok;
+  } else {
+    active = slot < a.B;
+    const int L = active ? a.seq_lens[slot] : 0;
+    if (active) pos = a.positions ? a.positions[slot] : (L > 0 ? L - 1 : 0);
+    tok = slot;
+    k_tok_out = (long)slot * a.max_seq + (L > 0 ? L - 1 : 0);
+    if (r >= a.H && L == 0) active = false;  // nothing to append to an empty sequence
+  }
+  const int nq = a.H, nk = a.k ? a.G : 0;
+  const bool is_q = r < nq, is_k = !is_q && r < nq + nk;
+  const T* src;
+  T* dst;
+  if (is_q) {
+    src = reinterpret_cast<const T*>(a.q) + (tok * a.H + r) * (long)D;
+    dst = reinterpret_cast<T*>(a.q_out) + (tok * a.H + r) * (long)D;
+  } else if (is_k) {
+    src = reinterpret_cast<const T*>(a.k) + (tok * a.G + (r - nq)) * (long)D;
+    dst = reinterpret_cast<T*>(a.k_out) + (k_tok_out * a.G + (r - nq)) * (long)D;
+  } else {
+    src = reinterpret_cast<const T*>(a.v) + (tok * a.G + (r - nq - nk)) * (long)D;
+    dst = reinterpret_cast<T*>(a.v_out) + (k_tok_out * a.G + (r - nq - nk)) * (long)D;
+  }
+
+  float x[8];
+  if (active) {
+    load8(src + e0, x);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = 0.f;
+  }
+  // all LPR lanes of a row share `active`, `is_q` and `is_k`, so the reduction below only
+  // mixes lanes of one row
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
+  ss = lane_group_sum<LPR>(ss);
+  const void* gam = is_q ? a.gq : (is_k ? a.gk : nullptr);
+  if (gam) {
+    float gw[8];
+    load8(reinterpret_cast<const T*>(gam) + e0, gw);
+    const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (x[i] * rinv) * gw[i];
+  }
+  if ((is_q || is_k) && a.use_rope) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      float c, sn;
+      rope_cs<T>((double)pos * a.omega[4 * ch + m], c, sn);
+      const float x0 = x[2 * m], x1 = x[2 * m + 1];
+      x[2 * m] = x0 * c - x1 * sn;
+      x[2 * m + 1] = x0 * sn + x1 * c;
+    }
+  }
+  if (active) store8(dst + e0, x);
+}
+
+template <typename T, int D>
+static hipError_t launch_prologue_t(const PrologueArgs& a, int slots, hipStream_t s) {
+  constexpr int ROWS_PER_BLOCK = 256 / (D / 8);
+  const long rows = (long)slots * (a.H + (a.k ? a.G : 0) + ((a.decode && a.v) ? a.G : 0));
+  const long grid = (rows + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
+  hipLaunchKernelGGL((qk_norm_rope_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_prologue(const PrologueArgs& a, int grid, int d, bool bf16, hipStream_t s) {
-  if (grid <= 0) return hipSuccess;
-  if (bf16) return d == 128 ? launch_prologue_t<bf16_t, 128>(a, grid, s)
-                            : launch_prologue_t<bf16_t, 64>(a, grid, s);
-  return d == 128 ? launch_prologue_t<float, 128>(a, grid, s)
-                  : launch_prologue_t<float, 64>(a, grid, s);
+hipError_t launch_prologue(const PrologueArgs& a, int slots, int d, bool bf16, hipStream_t s) {
+  if (slots <= 0) return hipSuccess;
+  if (bf16) return d == 128 ? launch_prologue_t<bf16_t, 128>(a, slots, s)
+                            : launch_prologue_t<bf16_t, 64>(a, slots, s);
+  return d == 128 ? launch_prologue_t<float, 128>(a, slots, s)
+                  : launch_prologue_t<float, 64>(a, slots, s);
 }
 
 }  // namespace gqa

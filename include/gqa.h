@@ -38,8 +38,10 @@
  *   - Errors found on the host are returned at once and nothing is enqueued:
  *       GQA_EINVAL    null required pointer, negative size, H, G or d <= 0, H % G != 0,
  *                     a device pointer not 16-byte aligned, an int array not 4-byte aligned;
- *       GQA_ENOTSUP   d not in {64, 128}, an unknown dtype, or a bf16 prefill whose
- *                     T * G * d * 2 exceeds 2^31 - 1 bytes (one sequence's K rows);
+ *       GQA_ENOTSUP   d not in {64, 128}, an unknown dtype, a bf16 prefill whose
+ *                     T * G * d * 2 exceeds 2^31 - 1 bytes (one sequence's K rows), or a
+ *                     decode whose max_seq * G * d * element size exceeds 2^31 - 1 bytes
+ *                     or max_seq exceeds 4096 * gqa_decode_split_keys();
  *       GQA_EWORKSPACE workspace smaller than gqa_workspace_bytes() or NULL when needed;
  *       GQA_EHIP      a HIP launch error.
  *     A batch with B == 0 or T == 0 is valid and enqueues nothing.  Device faults show up
