@@ -219,7 +219,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 // In the 16x16 accumulator lane l owns head l%16, so a head's online softmax lives in the 4
 // lanes l%16 + 16q. The reference max only moves when a probability would exceed 2^32 (the
 // same lazy rule as the prefill kernel). Each of the 4 waves covers a quarter of the split
-// with its own state; the states merge through LDS at the end.
+// with its own state, keeping two 32-key steps of loads in flight (double-buffered V in LDS,
+// K in registers); the states merge through LDS at the end.
 namespace {
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -232,7 +233,7 @@ __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 // values addressed by lanes 4j + i/4 of that block, j = 0..3.
 __device__ __forceinline__ u32x2_t ds_read_tr16(const char* lds) {
   typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)lds);
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)const_cast<char*>(lds));
   return __builtin_bit_cast(u32x2_t, v);
 }
 
@@ -253,15 +254,22 @@ __global__ __launch_bounds__(256, 2) void decode_split_mfma_kernel(DecodeArgs a)
   constexpr int NDMA = SUBB / 1024;         // 1 KB DMA instructions per sub-tile
   constexpr int DCH = D / 8;                // 16-byte chunks per row
   constexpr int NHEAD = 16 * HT;
-  constexpr int MERGEB = 4 * NHEAD * (D + 2) * 4;
-  constexpr int SMEMB = (4 * SUBB > MERGEB) ? 4 * SUBB : MERGEB;
-  __shared__ __attribute__((aligned(16))) char smem[SMEMB];
+  static_assert(4 * 16 * D * 4 <= 4 * SUBB, "merge scratch of one head tile fits a V buffer");
+  static_assert(HT <= 2, "one merge tile per V buffer");
+  // The two V buffers of every wave are separate LDS objects, so the compiler can tell that
+  // the DMA into one never feeds reads of the other and keeps its waits exact.
+  __shared__ __attribute__((aligned(16))) char vb0[4 * SUBB];
+  __shared__ __attribute__((aligned(16))) char vb1[4 * SUBB];
+  __shared__ float sm_ml[2][4][NHEAD];
 
-  const int s = blockIdx.x;
+  // grid: x = (group, head tile) fastest, y = split, z = sequence. The G workgroups of one
+  // split run side by side and read the same token rows of the cache (one row holds all G
+  // groups), which keeps DRAM pages open.
+  const int s = blockIdx.y;
   const int b = blockIdx.z;
   const int nht = (a.h + NHEAD - 1) / NHEAD;
-  const int g = blockIdx.y / nht;
-  const int head0 = (blockIdx.y % nht) * NHEAD;  // first head (inside the group) of this block
+  const int g = blockIdx.x / nht;
+  const int head0 = (blockIdx.x % nht) * NHEAD;  // first head (inside the group) of this block
   const int L = a.seq_lens[b];
   const int k0 = s * kDecodeSplit;
   if (k0 >= L) return;
@@ -306,28 +314,32 @@ __global__ __launch_bounds__(256, 2) void decode_split_mfma_kernel(DecodeArgs a)
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) o[ht][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  char* vbuf = smem + wave * SUBB;
+  char* const vbw[2] = {vb0 + wave * SUBB, vb1 + wave * SUBB};  // this wave's two V buffers
   const int kw0 = k0 + wave * KPW;
   const int kw1 = (kw0 + KPW < k1) ? kw0 + KPW : k1;
   const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
 
-  for (int kb = kw0; kb < kw1; kb += SUB) {
-    // V rows kb..kb+31 -> LDS. DMA instruction n fills rows n*RPD .. (RPD = rows per KB); lane
-    // slot pos of row r receives logical chunk pos ^ v_swz(r).
+  // Loads of one 32-key step: V rows by DMA into buffer `buf` (instruction n fills rows
+  // n * RPD.., lane slot pos of row r receives logical chunk pos ^ v_swz(r)), K rows into
+  // A-operand registers (tile tt: key kb + 16 tt + l16, d = 32 st + 8 q4 + [0, 8)).
+  // 2 * KSTEP + NDMA = 16 vector-memory instructions per step (D = 128).
+  u32x4_t kr[2][2][KSTEP];
+  auto issue = [&](int kb, int buf, u32x4_t (&k)[2][KSTEP]) {
 #pragma unroll
     for (int n = 0; n < NDMA; ++n) {
       const int r = n * (1024 / ROWB) + lane / DCH;
       const int c = (lane % DCH) ^ v_swz(r);
-      dma16(vrs, vbuf + n * 1024, (kb + r) * row_stride + c * 16, 0);
+      dma16(vrs, vbw[buf] + n * 1024, (kb + r) * row_stride + c * 16, 0);
     }
-    // K rows as A operands: tile tt holds keys kb + 16 tt + l16, d = 32 st + 8 q4 + [0, 8)
-    u32x4_t kr[2][KSTEP];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int st = 0; st < KSTEP; ++st)
-        kr[tt][st] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+        k[tt][st] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
             krs, (kb + 16 * tt + l16) * row_stride + (32 * st + 8 * q4) * 2, 0, 0));
+  };
+
+  auto step = [&](int kb, int buf, const u32x4_t (&k)[2][KSTEP], bool more) {
     // ---- S^T: keys (kb + 16 tt + 4 q4 + i) x heads
     f32x4_t sc[2][HT];
 #pragma unroll
@@ -336,7 +348,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_mfma_kernel(DecodeArgs a)
       for (int ht = 0; ht < HT; ++ht) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int st = 0; st < KSTEP; ++st) acc = mfma16(as_bf16x8(kr[tt][st]), qf[ht][st], acc);
+        for (int st = 0; st < KSTEP; ++st) acc = mfma16(as_bf16x8(k[tt][st]), qf[ht][st], acc);
         sc[tt][ht] = acc;
       }
     if (kb + SUB > kw1) {  // the last step of the sequence: keys >= kw1 are not there
@@ -386,9 +398,16 @@ __global__ __launch_bounds__(256, 2) void decode_split_mfma_kernel(DecodeArgs a)
       l_run[ht] += ls;
       pb[ht] = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
     }
+    // ---- this step's V DMA must have landed: only the next step's 16 loads may still be
+    // outstanding (vmcnt(16)), or none at the last step (vmcnt(0))
+    if (more) {
+      __builtin_amdgcn_s_waitcnt(0x4F70);
+    } else {
+      wait_vmem();
+    }
     // ---- O^T += V^T P^T; V^T operand: lane (d = 16 mt + l16) gets keys 4 q4 + 0..3 from the
     // first transposing read and 16 + 4 q4 + 0..3 from the second
-    wait_vmem();
+    const char* vbuf = vbw[buf];
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
       const int r0 = 4 * q4 + (l16 >> 2);
@@ -400,40 +419,60 @@ __global__ __launch_bounds__(256, 2) void decode_split_mfma_kernel(DecodeArgs a)
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) o[ht][mt] = mfma16(va, pb[ht], o[ht][mt]);
     }
+  };
+
+  // two steps in flight per wave: step u + 1's loads go out before step u computes. Inside
+  // the loop every issue is unconditional, so the wait counts the compiler derives for the K
+  // registers stay exact (a skipped issue on some path would make it wait for everything).
+  const int nsteps = (kw1 - kw0 + SUB - 1) / SUB;
+  if (nsteps > 0) issue(kw0, 0, kr[0]);
+  int u = 0;
+  for (; u + 2 < nsteps; u += 2) {
+    issue(kw0 + (u + 1) * SUB, 1, kr[1]);
+    step(kw0 + u * SUB, 0, kr[0], true);
+    issue(kw0 + (u + 2) * SUB, 0, kr[0]);
+    step(kw0 + (u + 1) * SUB, 1, kr[1], true);
+  }
+  if (u + 1 < nsteps) {
+    issue(kw0 + (u + 1) * SUB, 1, kr[1]);
+    step(kw0 + u * SUB, 0, kr[0], true);
+    step(kw0 + (u + 1) * SUB, 1, kr[1], false);
+  } else if (u < nsteps) {
+    step(kw0 + u * SUB, 0, kr[0], false);
   }
 
-  // ---- merge the 4 waves' states; layout sm_m[w][head], sm_l[w][head], sm_o[w][head][d]
-  __syncthreads();  // staged V no longer needed: reuse LDS
-  float* sm_m = reinterpret_cast<float*>(smem);
-  float* sm_l = sm_m + 4 * NHEAD;
-  float* sm_o = sm_l + 4 * NHEAD;
+  // ---- merge the 4 waves' states: sm_ml[0|1][w][head] = (m, l), and the O tile of head
+  // tile ht as [w][16][D] floats in V buffer ht (staged V is no longer needed)
+  __syncthreads();
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
     float lt = l_run[ht] + xor_shfl(l_run[ht], 16);
     lt += xor_shfl(lt, 32);
     const int hh = 16 * ht + l16;
     if (q4 == 0) {
-      sm_m[wave * NHEAD + hh] = m_run[ht];
-      sm_l[wave * NHEAD + hh] = lt;
+      sm_ml[0][wave][hh] = m_run[ht];
+      sm_ml[1][wave][hh] = lt;
     }
+    float* sm_o = reinterpret_cast<float*>(ht == 0 ? vb0 : vb1);
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm_o[(wave * NHEAD + hh) * D + 16 * mt + 4 * q4 + i] = o[ht][mt][i];
+      for (int i = 0; i < 4; ++i) sm_o[(wave * 16 + l16) * D + 16 * mt + 4 * q4 + i] = o[ht][mt][i];
   }
   __syncthreads();
   const int nh = (h - head0 < NHEAD) ? h - head0 : NHEAD;
   for (int idx = tid; idx < nh * D; idx += 256) {
     const int hh = idx / D, d = idx % D;
+    const float* sm_o = reinterpret_cast<const float*>(hh < 16 ? vb0 : vb1);
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w * NHEAD + hh]);
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_ml[0][w][hh]);
     float Ls = 0.f, Os = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float wt = __builtin_amdgcn_exp2f(sm_m[w * NHEAD + hh] - M);  // empty waves: 0
-      Ls = fmaf(sm_l[w * NHEAD + hh], wt, Ls);
-      Os = fmaf(sm_o[(w * NHEAD + hh) * D + d], wt, Os);
+      const float wt = __builtin_amdgcn_exp2f(sm_ml[0][w][hh] - M);  // empty waves: 0
+      Ls = fmaf(sm_ml[1][w][hh], wt, Ls);
+      Os = fmaf(sm_o[(w * 16 + (hh & 15)) * D + d], wt, Os);
     }
     const long pidx = ((long)b * a.H + (long)g * h + head0 + hh) * a.nsplit + s;
     a.part_o[pidx * D + d] = Os;
@@ -516,7 +555,7 @@ static hipError_t combine_td(const DecodeArgs& a, hipStream_t s) {
 template <int D, int HT>
 static hipError_t launch_split_mfma(const DecodeArgs& a, hipStream_t s) {
   const int nht = (a.h + 16 * HT - 1) / (16 * HT);
-  const dim3 grid(a.nsplit, a.G * nht, a.B);
+  const dim3 grid(a.G * nht, a.nsplit, a.B);
   hipLaunchKernelGGL((decode_split_mfma_kernel<D, HT>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -95,9 +95,11 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 
 // 16 bytes per lane from a buffer straight into LDS: lane i lands at lds + 16 i (the LDS
 // address is taken from the first lane, so it must be the same for the whole wave).
+// (A plain address-space cast keeps the pointer's provenance, so alias analysis can tell
+// which LDS array a DMA writes.)
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, const char* lds, int voff, int soff) {
   typedef __attribute__((address_space(3))) void lds_void;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(uintptr_t)lds, 16, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)const_cast<char*>(lds), 16, voff, soff, 0, 0);
 }
 
 // Sum over aligned groups of W consecutive lanes (W a power of two <= 64).
@@ -155,7 +157,7 @@ struct DecodeArgs {
   float scale_log2e;
 };
 
-constexpr int kDecodeSplit = 512;        // keys per split of the decode pass
+constexpr int kDecodeSplit = 1024;       // keys per split of the decode pass
 constexpr int kMaxCombineSplits = 4096;  // splits per sequence the combine pass can merge
 
 }  // namespace gqa

@@ -34,7 +34,9 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 FP32_PEAK_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
 
-WORKLOADS = ("default", "tiny_f32", "prefill_4k", "varlen", "decode", "long_g4", "long_g1")
+WORKLOADS = ("default", "tiny_f32", "prefill_4k", "varlen", "decode", "long_g4", "long_g1",
+             "copy_calibration")
+COPY_BYTES = 1 << 30  # bytes read (and written) per step of the copy calibration
 
 
 def log(*a):
@@ -163,6 +165,26 @@ def timed(fn, steps, warmup):
     return wall, call_ms, kern_ms
 
 
+def copy_calibration(steps, warmup):
+    """A plain device-to-device copy of COPY_BYTES per step (torch's copy kernel). Profiled
+    with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, it gives the factor that turns those
+    counters into HBM bytes."""
+    import torch
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    return {"metric": "device copy GB/s (calibration)", "value": round(2 * COPY_BYTES / ms / 1e6, 2),
+            "unit": "GB/s", "bytes_read_per_step": COPY_BYTES, "bytes_written_per_step": COPY_BYTES,
+            "ms_per_step": round(ms, 4), "steps": steps, "n_gpus": 1}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +202,9 @@ def main(argv=None):
     import torch
     import workloads as W
     log(f"bench: workload={args.workload} steps={args.steps} warmup={args.warmup}")
+    if args.workload == "copy_calibration":
+        print(json.dumps(copy_calibration(args.steps, args.warmup)), flush=True)
+        return 0
     torch.cuda.init()
     dev_name = torch.cuda.get_device_name(0)
 

@@ -28,15 +28,21 @@ def test_decode_64_sequences_sampled():
         assert np.array_equal(to_f64(dev["v_cache"][b, L - 1]), v_slot)
 
 
-EDGE_LENS = [0, 1, 2, 511, 512, 513, 1024, 1500, 3000]
+def edge_lens():
+    """Lengths around the split-KV partition: empty, tiny, both sides of one and two splits,
+    a quarter split (one wave's share), and a ragged multi-split length."""
+    import attention_head_qk_amd as gqa
+    S = gqa.decode_split_keys()
+    return [0, 1, 2, 31, 33, S // 4 - 1, S // 4 + 1, S - 1, S, S + 1, 2 * S, 2 * S + 37, 3 * S - 5]
 
 
 @pytest.mark.parametrize("dtype", [W.BF16, W.F32])
 @pytest.mark.parametrize("H,G,d", [(32, 8, 128), (12, 4, 128), (8, 8, 64), (16, 1, 128),
-                                   (6, 2, 64)])
+                                   (6, 2, 64), (40, 1, 128)])
 def test_decode_edge_lengths(dtype, H, G, d):
-    case = W.make_decode("edge", 61 + H + G + d, B=len(EDGE_LENS), max_seq=3072, H=H, G=G, d=d,
-                         dtype=dtype, seq_lens=EDGE_LENS)
+    EDGE_LENS = edge_lens()
+    case = W.make_decode("edge", 61 + H + G + d, B=len(EDGE_LENS), max_seq=max(EDGE_LENS), H=H,
+                         G=G, d=d, dtype=dtype, seq_lens=EDGE_LENS)
     say("decode edges", dtype, H, G, d)
     dev = device_decode_inputs(case, fill_invalid=float("nan"))
     out = to_f64(run_decode(case, dev))
