@@ -39,6 +39,37 @@ WORKLOADS = ("default", "tiny_f32", "prefill_4k", "varlen", "decode", "long_g4",
 COPY_BYTES = 1 << 30  # bytes read (and written) per step of the copy calibration
 
 
+TRAFFIC_RECORDS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the rocprofv3 FETCH_SIZE /
+    WRITE_SIZE record kept in profiles/ (KiB per dispatch, each scaled by the factor the same
+    counter gives for a plain copy of known size). None when there is no record, or when the
+    kernel's sources have changed since the counters were taken (sha256 of those files)."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_RECORDS).read()
+    except OSError:
+        return None
+    for line in text.splitlines():
+        line = line.strip().strip("`")
+        if not line.startswith("record:"):
+            continue
+        rec = dict(kv.split("=", 1) for kv in line[len("record:"):].split())
+        if rec.get("kernel") != kernel or rec.get("workload") != workload:
+            continue
+        h = hashlib.sha256()
+        for rel in rec["sources"].split(","):
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != rec["sha256"]:
+            return None
+        return (float(rec["fetch_kib"]) * float(rec["fetch_factor"]) +
+                float(rec["write_kib"]) * float(rec["write_factor"])) * 1024.0
+    return None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -255,11 +286,13 @@ def main(argv=None):
         tf_call = pre.work / (call_ms * 1e-3) / 1e12
         tf_kern = pre.work / (kern_ms * 1e-3) / 1e12
         peak = FP32_PEAK_TFLOPS if c.dtype == W.F32 else MFMA_BF16_PEAK_TFLOPS
+        kname = "prefill_bf16_kernel" if c.dtype == W.BF16 else "prefill_f32_kernel"
         line.update({"value": round(tf_call, 3), "unit": "TFLOP/s",
                      "dtype": "f32" if c.dtype == W.F32 else "bf16"})
         line["roofline"] = {"bound": "mfma", "achieved": round(tf_kern, 3), "peak": peak,
-                            "unit": "TFLOP/s", "frac": round(tf_kern / peak, 4), "traffic": None,
-                            "kernel": "prefill_bf16_kernel" if c.dtype == W.BF16 else "prefill_f32_kernel",
+                            "unit": "TFLOP/s", "frac": round(tf_kern / peak, 4),
+                            "traffic": measured_traffic(kname, c.name),
+                            "kernel": kname,
                             "kernel_ms": round(kern_ms, 5), "flops_per_launch": c.flops}
         line["prefill"] = {"ms": round(call_ms, 5), "tflops": round(tf_call, 3),
                            "frac_of_peak": round(tf_call / peak, 4)}
@@ -275,8 +308,9 @@ def main(argv=None):
                           "bytes": dec.work}
         line["roofline_decode"] = {"bound": "hbm", "achieved": round(gbs_kern, 2),
                                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                   "frac": round(gbs_kern / HBM_PEAK_GBS, 4), "traffic": None,
-                                   "kernel": "decode_split_kernel", "kernel_ms": round(kern_ms, 5)}
+                                   "frac": round(gbs_kern / HBM_PEAK_GBS, 4),
+                                   "traffic": measured_traffic("decode_split_mfma_kernel", c.name),
+                                   "kernel": "decode_split_mfma_kernel", "kernel_ms": round(kern_ms, 5)}
         cfg["decode"] = {"name": c.name, "B": c.B, "sum_L": int(c.seq_lens.sum()), "max_seq": c.max_seq,
                          "H": c.H, "G": c.G, "d": c.d, "seed": c.seed}
         if pre is None:
