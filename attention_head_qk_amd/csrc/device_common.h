@@ -102,6 +102,25 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, const char* lds
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)const_cast<char*>(lds), 16, voff, soff, 0, 0);
 }
 
+// cos and sin of the RoPE angle phi = pos * omega_j: the angle is reduced to revolutions in
+// fp64 (exact to ~1e-12 rad at pos 32767). bf16 outputs then take the hardware sin/cos of the
+// fp32 revolution count (abs error ~1e-6, far below bf16 rounding), fp32 outputs an fp64
+// sincos.
+template <bool BF16>
+__device__ __forceinline__ void rope_cos_sin(double phi, float& c, float& s) {
+  const double rev = phi * 0.15915494309189533577;  // 1 / (2 pi)
+  if constexpr (BF16) {
+    const float r = (float)(rev - floor(rev));
+    s = __builtin_amdgcn_sinf(r);  // sin(2 pi r)
+    c = __builtin_amdgcn_cosf(r);
+  } else {
+    double sd, cd;
+    sincos(phi - floor(rev) * 6.283185307179586476925286766559, &sd, &cd);
+    s = (float)sd;
+    c = (float)cd;
+  }
+}
+
 // Sum over aligned groups of W consecutive lanes (W a power of two <= 64).
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
@@ -132,7 +151,12 @@ struct PrologueArgs {
 };
 
 struct PrefillArgs {
-  const void* qt;     // [N, H, D] normalised, rotated Q
+  const void* qt;     // fp32 kernel: [N, H, D] normalised, rotated Q
+  const void* q;      // bf16 kernel: [N, H, D] raw Q, normalised and rotated in the kernel
+  const int32_t* positions;  // bf16 kernel: RoPE positions [N] or null (index in sequence)
+  const void* gq;     // bf16 kernel: gamma_q [D] or null (no norm)
+  float eps;
+  int use_rope;
   const void* kt;     // [N, G, D] normalised, rotated K
   const void* v;      // [N, G, D]
   void* out;          // [N, H, D]
@@ -143,6 +167,7 @@ struct PrefillArgs {
   int zigzag;         // 1: pair heavy and light blocks (see the prefill kernel)
   float scale;        // score scale (1/sqrt(d) by default)
   float scale_log2e;  // scale * log2(e)
+  double omega[kMaxHalfD];  // bf16 kernel: theta^(-2j/d), computed on the host in fp64
 };
 
 struct DecodeArgs {

@@ -49,7 +49,8 @@ float eff_scale(const gqa_params* p, int d) {
   return p->scale > 0.f ? p->scale : (float)(1.0 / std::sqrt((double)d));
 }
 
-void fill_rope(gqa::PrologueArgs& a, const gqa_params* p, int d) {
+template <typename Args>
+void fill_rope(Args& a, const gqa_params* p, int d) {
   a.use_rope = p->rope_theta > 0.0 ? 1 : 0;
   for (int j = 0; j < gqa::kMaxHalfD; ++j)
     a.omega[j] = (a.use_rope && j < d / 2) ? std::pow(p->rope_theta, -2.0 * j / d) : 0.0;
@@ -103,8 +104,10 @@ size_t gqa_workspace_bytes(int op, int B, int T_or_max_seq, int H, int G, int d,
   if (B < 0 || T_or_max_seq < 0 || check_heads(H, G, d) != GQA_OK || !dtype_ok(dtype)) return 0;
   const size_t es = elem_size(dtype);
   if (op == GQA_OP_PREFILL) {
+    // k~ [N, G, d]; the fp32 path also stages q~ [N, H, d] (the bf16 attention kernel
+    // normalises and rotates Q itself)
     const size_t N = (size_t)B * (size_t)T_or_max_seq;
-    return align_up(N * H * d * es) + align_up(N * G * d * es);
+    return (dtype == GQA_BF16 ? 0 : align_up(N * H * d * es)) + align_up(N * G * d * es);
   }
   if (op == GQA_OP_DECODE) {
     const size_t ns = (size_t)decode_nsplit(T_or_max_seq);
@@ -137,12 +140,12 @@ gqa_status gqa_prefill(const void* q, const void* k, const void* v, const int32_
   const size_t N = (size_t)B * T;
   hipStream_t stream = reinterpret_cast<hipStream_t>(p->stream);
   char* ws = static_cast<char*>(p->workspace);
-  void* qt = ws;
-  void* kt = p->k_out ? p->k_out : ws + align_up(N * H * d * es);
+  void* qt = bf16 ? nullptr : ws;
+  void* kt = p->k_out ? p->k_out : ws + (bf16 ? 0 : align_up(N * H * d * es));
   (void)hipGetLastError();
 
   gqa::PrologueArgs pa{};
-  pa.q = q;
+  pa.q = bf16 ? nullptr : q;
   pa.k = k;
   pa.q_out = qt;
   pa.k_out = kt;
@@ -161,6 +164,11 @@ gqa_status gqa_prefill(const void* q, const void* k, const void* v, const int32_
 
   gqa::PrefillArgs fa{};
   fa.qt = qt;
+  fa.q = q;
+  fa.positions = positions;
+  fa.gq = p->q_norm_w;
+  fa.eps = p->eps;
+  fill_rope(fa, p, d);
   fa.kt = kt;
   fa.v = v;
   fa.out = out;

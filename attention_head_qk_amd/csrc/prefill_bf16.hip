@@ -4,8 +4,9 @@
 //   out = softmax(q k^T * scale + M) v, M = -inf above the diagonal, the row max subtracted
 // -- zhanghao0806.com "Qwen3系列1-理论基础&真实结构", D1-4 (formula), D1-5 (mask), D1-2
 // (stable softmax), D2-3 (h query heads of a group share one K/V head); ewbang.com
-// "深入剖析Qwen3模型架构" 3.1.2 (head i reads K/V head floor(i/h)). Q and K arrive already
-// normalised and rotated by the prologue kernel.
+// "深入剖析Qwen3模型架构" 3.1.2 (head i reads K/V head floor(i/h)). K arrives normalised and
+// rotated by the prologue kernel; each workgroup applies the same per-head RMSNorm and RoPE
+// (D2-1, D2-2) to its own Q columns as it loads them.
 //
 // Design for CDNA4 (not a port of any FlashAttention code):
 // * Columns. A workgroup owns 128 "columns"; a column is one (query position, head) pair of
@@ -113,15 +114,55 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   const int p_wlo = (wcol < ncol) ? (int)(wcol / h) : Tb - 1;  // lowest position in the wave
   const int plim = a.causal ? pcol : 0x7fffffff;
 
-  // ---- Q^T (B operand): step st holds d = 16 st + 8 grp + [0, 8) of this lane's column
+  // ---- Q^T (B operand): step st holds d = 16 st + 8 grp + [0, 8) of this lane's column; the
+  // rest of the row is in the partner lane l^32. The row is normalised (per-head RMSNorm with
+  // gamma_q) and rotated (RoPE at the column's position) here in fp32, then rounded to bf16:
+  // the same arithmetic as the prologue kernel, without a trip through HBM.
   bf16x8_t qf[NST];
   {
-    const bf16_t* qp = reinterpret_cast<const bf16_t*>(a.qt) + ((long)(seq0 + pcol) * a.H + head) * D + 8 * grp;
+    const long qrow = ((long)(seq0 + pcol) * a.H + head) * D + 8 * grp;
+    const bf16_t* qp = reinterpret_cast<const bf16_t*>(a.q) + qrow;
+    u32x4_t raw[NST];
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
-      u32x4_t w = {0u, 0u, 0u, 0u};
-      if (cvalid) w = *reinterpret_cast<const u32x4_t*>(qp + 16 * st);
-      qf[st] = as_bf16x8(w);
+      raw[st] = u32x4_t{0u, 0u, 0u, 0u};
+      if (cvalid) raw[st] = *reinterpret_cast<const u32x4_t*>(qp + 16 * st);
+    }
+    float rinv = 1.f;
+    if (a.gq) {
+      float ss = 0.f;
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        float x[8];
+        unpack8(raw[st], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+      }
+      ss += xor_shfl(ss, 32);
+      rinv = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
+    }
+    const int pos = a.positions ? a.positions[seq0 + pcol] : pcol;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      float x[8];
+      unpack8(raw[st], x);
+      if (a.gq) {
+        float gw[8];
+        load8(reinterpret_cast<const bf16_t*>(a.gq) + 16 * st + 8 * grp, gw);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (x[e] * rinv) * gw[e];
+      }
+      if (a.use_rope) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          float c, sn;
+          rope_cos_sin<true>((double)pos * a.omega[8 * st + 4 * grp + m], c, sn);
+          const float x0 = x[2 * m], x1 = x[2 * m + 1];
+          x[2 * m] = x0 * c - x1 * sn;
+          x[2 * m + 1] = x0 * sn + x1 * c;
+        }
+      }
+      qf[st] = as_bf16x8(pack8(x));
     }
   }
 

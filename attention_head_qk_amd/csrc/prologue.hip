@@ -10,10 +10,8 @@
 // chunk (4 rotation pairs) of one head row of one token, so the whole tensor is in flight at
 // once; d/8 lanes cover a row with one coalesced read, the sum of squares is reduced across
 // them with DPP row permutes, and each lane evaluates its own four angles (cheap next to the
-// row's HBM traffic). Angles: pos * omega_j and its reduction to revolutions
-// are done in fp64 (exact to ~1e-12 rad at pos 32767); bf16 outputs then take the hardware
-// sin/cos of the fp32 revolution count (abs error ~1e-6, far below bf16 rounding), fp32
-// outputs an fp64 sincos.
+// row's HBM traffic; rope_cos_sin gives the precision). With q null (the bf16 prefill, whose
+// attention kernel prepares Q itself) only K rows are processed.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -37,28 +35,13 @@ __device__ __forceinline__ float lane_group_sum(float v) {
   return v;
 }
 
-template <typename T>
-__device__ __forceinline__ void rope_cs(double phi, float& c, float& s) {
-  // revolutions in [0, 1), reduced in fp64
-  const double rev = phi * 0.15915494309189533577;  // 1 / (2 pi)
-  const float r = (float)(rev - floor(rev));
-  if constexpr (sizeof(T) == 2) {
-    s = __builtin_amdgcn_sinf(r);  // sin(2 pi r)
-    c = __builtin_amdgcn_cosf(r);
-  } else {
-    double sd, cd;
-    sincos(phi - floor(rev) * 6.283185307179586476925286766559, &sd, &cd);
-    s = (float)sd;
-    c = (float)cd;
-  }
-}
-
 }  // namespace
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void qk_norm_rope_kernel(PrologueArgs a) {
   constexpr int LPR = D / 8;  // lanes per head row (8 elements = one 16-byte bf16 chunk each)
-  const int rows_per_token = a.H + (a.k ? a.G : 0) + ((a.decode && a.v) ? a.G : 0);
+  const int nq = a.q ? a.H : 0, nk = a.k ? a.G : 0;
+  const int rows_per_token = nq + nk + ((a.decode && a.v) ? a.G : 0);
   const long item = (long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;  // (token slot, row)
   const int ch = threadIdx.x % LPR;
   const int e0 = ch * 8;
@@ -90,7 +73,6 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(PrologueArgs a) {
     k_tok_out = (long)slot * a.max_seq + (L > 0 ? L - 1 : 0);
     if (r >= a.H && L == 0) active = false;  // nothing to append to an empty sequence
   }
-  const int nq = a.H, nk = a.k ? a.G : 0;
   const bool is_q = r < nq, is_k = !is_q && r < nq + nk;
   const T* src;
   T* dst;
@@ -130,7 +112,7 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(PrologueArgs a) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       float c, sn;
-      rope_cs<T>((double)pos * a.omega[4 * ch + m], c, sn);
+      rope_cos_sin<sizeof(T) == 2>((double)pos * a.omega[4 * ch + m], c, sn);
       const float x0 = x[2 * m], x1 = x[2 * m + 1];
       x[2 * m] = x0 * c - x1 * sn;
       x[2 * m + 1] = x0 * sn + x1 * c;
@@ -142,8 +124,9 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(PrologueArgs a) {
 template <typename T, int D>
 static hipError_t launch_prologue_t(const PrologueArgs& a, int slots, hipStream_t s) {
   constexpr int ROWS_PER_BLOCK = 256 / (D / 8);
-  const long rows = (long)slots * (a.H + (a.k ? a.G : 0) + ((a.decode && a.v) ? a.G : 0));
+  const long rows = (long)slots * ((a.q ? a.H : 0) + (a.k ? a.G : 0) + ((a.decode && a.v) ? a.G : 0));
   const long grid = (rows + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
+  if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((qk_norm_rope_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -173,8 +173,9 @@ def cpu_baseline(case, budget_s=12.0):
 
 
 def timed(fn, steps, warmup):
-    """Warm up, then time ``steps`` calls with events around each whole call and around the
-    main kernel (recorded by the library on the launch stream)."""
+    """Warm up, then time ``steps`` calls with events around each whole call, and ``steps``
+    more with events around the main kernel only (recorded by the library on the launch
+    stream), so that neither measurement carries the other's event records."""
     import torch
     for _ in range(warmup):
         fn()
@@ -187,10 +188,13 @@ def timed(fn, steps, warmup):
     t0 = time.perf_counter()
     for e in ev:
         e[0].record()
-        fn(prof=(e[1], e[2]))
+        fn()
         e[3].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    for e in ev:
+        fn(prof=(e[1], e[2]))
+    torch.cuda.synchronize()
     call_ms = sum(e[0].elapsed_time(e[3]) for e in ev) / steps
     kern_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
     return wall, call_ms, kern_ms
