@@ -19,19 +19,24 @@
 //   of a column lives in one lane (plus its partner lane l^32 for the other half of the
 //   keys), and the bf16-packed probabilities already sit in the B-operand layout of the
 //   second product O^T = V^T P^T: no LDS round trip for P.
-// * K tiles go global -> LDS by DMA (16-byte buffer loads into LDS), XOR-swizzled by 16-byte
-//   chunk. The A operand of O^T needs 8 consecutive keys per lane, so V tiles are loaded
-//   into registers and transposed on their way into LDS (4 keys x 8 d per thread, v_perm_b32
-//   regroups the halves, 8-byte stores), with the key order inside each 16-key step permuted
-//   so the 8 keys a lane needs are one 16-byte read. Both layouts are bank-conflict free for
-//   the reads and writes they see. Buffer descriptors bound each sequence, so rows past its
-//   end read as zero without per-load tests, and every LDS address is computed once.
-// * Pipeline. LDS is double-buffered: the loads of tile t+1 are issued before the MFMAs of
-//   tile t and the V^T store follows them; one barrier per tile.
-// * Softmax in base 2 with scale*log2(e) folded into one FMA per score. The reference max
-//   of a column only moves when the probabilities it gives would exceed 2^32 (a wave-uniform
-//   test on the tile sums), so the common tile needs neither a max nor an O rescale; the
-//   result is unchanged because softmax does not depend on the subtracted constant.
+// * K and V tiles go global -> LDS by DMA (16-byte buffer loads into LDS), each row's 16-byte
+//   chunks XOR-swizzled. The A operand of O^T (V^T: 8 keys of one d per lane) comes out of
+//   the natural [key][d] layout through transposing reads (ds_read_b64_tr_b16), so V needs
+//   no registers or VALU on its way in. Every read pattern is bank-conflict free. Buffer
+//   descriptors bound each sequence, so rows past its end read as zero without per-load
+//   tests, and every LDS address is computed once.
+// * MFMA chains. An MFMA that accumulates onto a result still in flight waits for it
+//   (~100 cycles for this shape on gfx950, against ~32 between independent issues), so both
+//   products keep four independent accumulators in flight: S^T splits each 32-key block's
+//   d-sum in two halves, O^T updates its four 32-row tiles in turn. Fragments are read one
+//   round ahead.
+// * Pipeline. LDS is double-buffered: the DMA of tile t+1 is issued before the MFMAs of tile t;
+//   one barrier per tile.
+// * Softmax in base 2: Q is pre-scaled by scale*log2(e), so scores come out in log2 units. The
+//   reference m of a column (P = 2^(s - m)) starts at 0 and only moves when a tile's
+//   probabilities would leave [2^-100, 2^32], so the common tile needs neither a max, a
+//   subtraction nor an O rescale; the result is unchanged because softmax does not depend on
+//   the subtracted constant.
 // * Scheduling. Blocks are issued heaviest first (descending position) so the causal
 //   triangle drains without a long tail; when the whole grid fits on the chip in about two
 //   rounds, heavy and light blocks are paired instead (zigzag). The group index is the
@@ -52,10 +57,22 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Swizzle of the 16-byte chunk index of a V^T row (8 chunks of 8 keys). It depends on d mod 32
-// only, so the 32-row tiles of one lane differ by a constant offset, and it is conflict-free
-// both for the MFMA reads (16 consecutive d) and for the transposing writes (one d per 16 lanes).
-__device__ __forceinline__ int vt_swz(int d) { return ((d >> 3) & 3) ^ (d & 7); }
+// Swizzle of the 16-byte chunk index of a V row in LDS (row = key). A transposing read of the
+// O^T product touches 8 rows (4 consecutive keys for each lane half) at 4 chunks of one 32-d
+// tile; the XOR moves those rows to 4 different 64-byte bank windows, so every read is two
+// bank cycles for its 512 bytes. It depends on the row's low bits only, which DMA instruction
+// and read-row offsets (multiples of 4 or 8 rows) leave unchanged.
+template <int D>
+__device__ __forceinline__ int v_swz(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+
+// ds_read_b64_tr_b16: inside every 16-lane block, lane i receives element i%4 of the 8-byte
+// values addressed by lanes 4j + i/4 of that block, j = 0..3.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2_t ds_read_tr16(const char* lds) {
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)const_cast<char*>(lds));
+  return __builtin_bit_cast(u32x2_t, v);
+}
 
 }  // namespace
 
@@ -69,7 +86,11 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int BUFBYTES = KBYTES + VBYTES;
   constexpr int KDMA = KBYTES / 1024 / 4;  // 1 KB DMA instructions per wave per K tile
   constexpr int KROWS_DMA = 1024 / (D * 2);  // K rows per DMA instruction
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUFBYTES];
+  // The two buffers (K tile then V tile each) are separate LDS objects, so the compiler can
+  // tell that the DMA into one never feeds reads of the other and keeps its waits exact.
+  __shared__ __attribute__((aligned(16))) char smem0[BUFBYTES];
+  __shared__ __attribute__((aligned(16))) char smem1[BUFBYTES];
+  auto lds_buf = [&](int BUF) -> char* { return BUF ? smem1 : smem0; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -116,8 +137,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
 
   // ---- Q^T (B operand): step st holds d = 16 st + 8 grp + [0, 8) of this lane's column; the
   // rest of the row is in the partner lane l^32. The row is normalised (per-head RMSNorm with
-  // gamma_q) and rotated (RoPE at the column's position) here in fp32, then rounded to bf16:
-  // the same arithmetic as the prologue kernel, without a trip through HBM.
+  // gamma_q) and rotated (RoPE at the column's position) here in fp32 -- the same arithmetic
+  // as the prologue kernel, without a trip through HBM -- then multiplied by scale * log2(e),
+  // so that the scores come out of the matrix cores in log2 units, and rounded to bf16.
   bf16x8_t qf[NST];
   {
     const long qrow = ((long)(seq0 + pcol) * a.H + head) * D + 8 * grp;
@@ -162,6 +184,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
           x[2 * m + 1] = x0 * sn + x1 * c;
         }
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= a.scale_log2e;
       qf[st] = as_bf16x8(pack8(x));
     }
   }
@@ -175,96 +199,104 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
 
   // K tile: DMA straight into LDS. DMA instruction n (= i*4 + wave) fills bytes
   // [n KB, (n+1) KB) of the tile; lane slot pos of row r receives logical chunk pos ^ (r % DCH),
-  // i.e. the tile is stored XOR-swizzled by 16-byte chunk.
-  int k_voff[KDMA];
-#pragma unroll
-  for (int i = 0; i < KDMA; ++i) {
-    const int n = i * 4 + wave;
-    const int r = n * KROWS_DMA + lane / DCH;
-    const int c = (lane % DCH) ^ (r % DCH);
-    k_voff[i] = r * row_bytes + c * 16;
-  }
-  // V tile: thread (vch = tid / 16, vq = tid % 16) loads keys 4vq..4vq+3 at d-chunk vch.
-  const bool vload = tid < (KT / 4) * DCH;
-  const int vch = tid >> 4, vq = tid & 15;
-  int v_voff[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) v_voff[kk] = (4 * vq + kk) * row_bytes + vch * 16;
-  // V^T destination of this thread: keys 4vq.. -> physical slot 32kb + 16half + 8gg + 4aa
-  int vt_woff[8];
+  // i.e. the tile is stored XOR-swizzled by 16-byte chunk. Row r = 4 KROWS_DMA i + r0 and
+  // r % DCH does not depend on i, so the i part goes into the scalar offset. (Buffer range
+  // checks include the scalar offset: rows past the sequence still read as zero.)
+  int k_voff;
   {
-    const int kb = vq >> 3, qi = vq & 7;
-    const int half = qi >> 2, aa = (qi >> 1) & 1, gg = qi & 1;
-    const int chunk = 4 * kb + 2 * half + gg;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 8 * vch + e;
-      vt_woff[e] = KBYTES + d * KT * 2 + ((chunk ^ vt_swz(d)) * 16) + 8 * aa;
-    }
+    const int r0 = wave * KROWS_DMA + lane / DCH;
+    static_assert((4 * KROWS_DMA) % DCH == 0, "the swizzle of a DMA row is the same for every i");
+    k_voff = r0 * row_bytes + ((lane % DCH) ^ (r0 % DCH)) * 16;
+  }
+  // V tile: DMA into LDS in natural [key][d] order (after K in the same buffer), each row's
+  // 16-byte chunks XOR-swizzled by v_swz; the row layout of the DMA is the same as K's.
+  int vd_voff;
+  {
+    const int r0 = wave * KROWS_DMA + lane / DCH;
+    vd_voff = r0 * row_bytes + ((lane % DCH) ^ v_swz<D>(r0)) * 16;
   }
   // LDS read offsets (the m-tile and buffer parts are compile-time offsets)
   int k_roff[NST];
 #pragma unroll
   for (int st = 0; st < NST; ++st) k_roff[st] = l32 * D * 2 + ((((2 * st + grp) ^ (l32 % DCH))) * 16);
-  int v_roff[2][2];
+  // O^T A operand (V^T, rows d = 32 mt + l32): two transposing reads per fragment. Lane l
+  // (s = l % 16, grp = l / 32) addresses key row 4 grp + s/4 (+ 32 kb + 16 hf + 8 rd, all
+  // immediate offsets) at d = 32 mt + 16 ((l / 16) & 1) + 4 (s % 4): it then receives keys
+  // 4 grp + 0..3 (rd = 0) and 8 + 4 grp + 0..3 (rd = 1) of its own d, the key order of the
+  // P^T operand.
+  int v_roff[NMT];
+  {
+    const int s16 = lane & 15;
+    const int row = 4 * grp + (s16 >> 2);
+    const int cl = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-      v_roff[kb][hf] = KBYTES + l32 * KT * 2 + (((4 * kb + 2 * hf + grp) ^ vt_swz(l32)) * 16);
-
-  u32x4_t vreg[4];
+    for (int mt = 0; mt < NMT; ++mt)
+      v_roff[mt] = KBYTES + row * D * 2 + (((4 * mt + cl) ^ v_swz<D>(row)) * 16) + 8 * (s16 & 1);
+  }
 
   // The buffer index is always a literal at the call sites, so after inlining every LDS
   // offset below folds into the instructions' immediate offset field.
-  auto issue_tile = [&](int BUF, int t) {
+  auto issue_k = [&](int BUF, int t) {  // K tile t -> LDS buffer BUF (DMA)
     const int soff = t * KT * row_bytes;
 #pragma unroll
     for (int i = 0; i < KDMA; ++i)
-      dma16(krs, smem + BUF * BUFBYTES + (i * 4 + wave) * 1024, k_voff[i], soff);
-    if (vload) {
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        vreg[kk] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, v_voff[kk], soff, 0));
-    }
+      dma16(krs, lds_buf(BUF) + (i * 4 + wave) * 1024, k_voff,
+            soff + i * 4 * KROWS_DMA * row_bytes);
   };
-
-  auto store_vt = [&](int BUF) {
-    if (vload) {
+  auto issue_v = [&](int BUF, int t) {  // V tile t -> LDS buffer BUF (DMA)
+    const int soff = t * KT * row_bytes;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // d = 8 vch + 2w (low halves of the four keys) and d + 1 (high halves)
-        const uint32_t lo01 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x05040100u);
-        const uint32_t lo23 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x05040100u);
-        const uint32_t hi01 = __builtin_amdgcn_perm(vreg[1][w], vreg[0][w], 0x07060302u);
-        const uint32_t hi23 = __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], 0x07060302u);
-        *reinterpret_cast<u32x2_t*>(smem + BUF * BUFBYTES + vt_woff[2 * w]) = u32x2_t{lo01, lo23};
-        *reinterpret_cast<u32x2_t*>(smem + BUF * BUFBYTES + vt_woff[2 * w + 1]) = u32x2_t{hi01, hi23};
-      }
-    }
+    for (int i = 0; i < KDMA; ++i)
+      dma16(vrs, lds_buf(BUF) + KBYTES + (i * 4 + wave) * 1024, vd_voff,
+            soff + i * 4 * KROWS_DMA * row_bytes);
   };
 
   f32x16_t o[NMT];
 #pragma unroll
   for (int mt = 0; mt < NMT; ++mt) o[mt] = f32x16_t{};
-  float m_run = -INFINITY;  // reference max of this column, log2 units
-  float l_run = 0.f;        // this lane's share of the running sum
-  const float sl2e = a.scale_log2e;
+  float m_run = 0.f;     // reference of this column (log2 units): P = 2^(s - m_run)
+  float l_run = 0.f;     // this lane's share of the running sum
+  bool shifted = false;  // wave-uniform: some column's reference has left 0
 
-  auto compute_tile = [&](int BUF, int t) {
-    const char* sb = smem + BUF * BUFBYTES;
-    // ---- S^T = K Q^T: two 32-key blocks
-    f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+  // ---- S^T = K Q^T for one tile (two 32-key blocks) from LDS buffer BUF. An MFMA that
+  // accumulates onto a result still in flight waits for it (~100 cycles for this shape,
+  // against ~32 between independent issues), so the d-sum of each block is split in two
+  // halves: four independent accumulators, added at the end.
+  auto s_product = [&](int BUF, f32x16_t (&s)[2]) {
+    const char* sb = lds_buf(BUF);
+    constexpr int HS = NST / 2;
+    f32x16_t s4[2][2];
 #pragma unroll
-    for (int st = 0; st < NST; ++st) {
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const u32x4_t kw = *reinterpret_cast<const u32x4_t*>(sb + k_roff[st] + mt * 32 * D * 2);
-        s[mt] = mfma32(as_bf16x8(kw), qf[st], s[mt]);
-      }
+      for (int hh = 0; hh < 2; ++hh) s4[mt][hh] = f32x16_t{};
+    // round r: one MFMA on each of the four accumulators, its K fragments read a round ahead
+    u32x4_t kf[2][4];
+    auto load = [&](int r, u32x4_t (&f)[4]) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          f[2 * hh + mt] = *reinterpret_cast<const u32x4_t*>(sb + k_roff[r + hh * HS] + mt * 32 * D * 2);
+    };
+    load(0, kf[0]);
+#pragma unroll
+    for (int r = 0; r < HS; ++r) {
+      if (r + 1 < HS) load(r + 1, kf[(r + 1) & 1]);
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          s4[mt][hh] = mfma32(as_bf16x8(kf[r & 1][2 * hh + mt]), qf[r + hh * HS], s4[mt][hh]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- mask: only tiles that reach past the wave's lowest position, or past the end.
-    // key = t0 + 32 mt + 8 (i/4) + 4 grp + i%4 is visible iff key <= min(plim, Tb - 1).
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) s[mt] = s4[mt][0] + s4[mt][1];
+  };
+
+  // ---- mask: only tiles that reach past the wave's lowest position, or past the end.
+  // key = t0 + 32 mt + 8 (i/4) + 4 grp + i%4 is visible iff key <= min(plim, Tb - 1).
+  auto mask_tile = [&](f32x16_t (&s)[2], int t) {
     const int t0 = t * KT;
     if ((a.causal && t0 + KT - 1 > p_wlo) || t0 + KT > Tb) {
       const int lim = (plim < Tb - 1 ? plim : Tb - 1) - t0 - 4 * grp;
@@ -275,84 +307,111 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
           if (32 * mt + 8 * (i >> 2) + (i & 3) > lim) s[mt][i] = -INFINITY;
       }
     }
-    // ---- probabilities against the column's reference max m_run (log2 units). The common
-    // case needs no max at all: P = 2^(s*c - m_run) is accepted while every lane's tile sum
-    // stays <= 2^32 (so every P does); otherwise (always on the first tile, where m_run is
-    // -inf) the wave takes the exact path: tile max, new reference, rescale O and l, redo P.
-    // The row sum is taken over the bf16-rounded P that also feeds the P.V product.
-    const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
-    uint32_t pk[2][8];
+  };
+
+  // ---- probabilities P = 2^(s - m_run); softmax does not depend on the reference m_run, it
+  // only keeps P in range. It starts at 0, so while it stays there P = 2^s needs no
+  // subtraction. A tile is accepted while every lane's tile sum is <= 2^32 (so no P or sum
+  // can overflow) and every column's running sum is >= 2^-100 (so its largest P is a normal
+  // number); otherwise the wave takes the exact path: the column max becomes the reference
+  // (never lower than before, unless nothing has been summed yet), O and l are rescaled, P is
+  // redone; once a reference has moved, the wave takes that path for every later tile. The
+  // row sum is taken over the bf16-rounded P that also feeds the P.V product.
+  const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+  auto probs = [&](const f32x16_t (&s)[2], uint32_t (&pk)[2][8], bool sub) {
     float ls = 0.f;
-    auto probs = [&]() {
-      ls = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * j], sl2e, -m_run));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * j + 1], sl2e, -m_run));
-          f32x2_t pp = {p0, p1};
-          const bf16x2_t pb2 = __builtin_convertvector(pp, bf16x2_t);
-          pk[kb][j] = __builtin_bit_cast(uint32_t, pb2);
-          ls = __builtin_amdgcn_fdot2_f32_bf16(pb2, one2, ls, false);
-        }
+      for (int j = 0; j < 8; ++j) {
+        const float x0 = sub ? s[kb][2 * j] - m_run : s[kb][2 * j];
+        const float x1 = sub ? s[kb][2 * j + 1] - m_run : s[kb][2 * j + 1];
+        f32x2_t pp = {__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1)};
+        const bf16x2_t pb2 = __builtin_convertvector(pp, bf16x2_t);
+        pk[kb][j] = __builtin_bit_cast(uint32_t, pb2);
+        ls = __builtin_amdgcn_fdot2_f32_bf16(pb2, one2, ls, false);
       }
-    };
-    probs();
-    if (__any(!(ls <= 0x1p32f))) {
-      float mx = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s[0][i], s[1][i]));
-      mx = fmaxf(mx, xor_shfl(mx, 32)) * sl2e;
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt) o[mt] *= alpha;
-      m_run = m_new;
-      probs();
     }
-    l_run += ls;
+    return ls;
+  };
+  auto rescale = [&](const f32x16_t (&s)[2]) {
+    float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s[0][i], s[1][i]));
+    mx = fmaxf(mx, xor_shfl(mx, 32));
+    const float l_col = l_run + xor_shfl(l_run, 32);  // the column's sum before this tile
+    float m_new = l_col > 0.f ? fmaxf(m_run, mx) : mx;
+    if (m_new == -INFINITY) m_new = m_run;  // no visible key yet: keep the reference
+    const float alpha = l_col > 0.f ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+    l_run *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) o[mt] *= alpha;
+    m_run = m_new;
+  };
+
+  // ---- O^T += V^T P^T from LDS buffer BUF: round (kb, hf) issues one MFMA on each of the
+  // NMT accumulators (independent chains), its V^T fragments read a round ahead
+  auto pv_product = [&](int BUF, const uint32_t (&pk)[2][8]) {
+    const char* sb = lds_buf(BUF);
     bf16x8_t pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
         pb[kb][hf] = as_bf16x8(u32x4_t{pk[kb][4 * hf], pk[kb][4 * hf + 1], pk[kb][4 * hf + 2], pk[kb][4 * hf + 3]});
-    // ---- O^T += V^T P^T
+    u32x4_t vf[2][NMT];
+    auto load = [&](int r, u32x4_t (&f)[NMT]) {  // r = 2 kb + hf
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const u32x4_t vw = *reinterpret_cast<const u32x4_t*>(sb + v_roff[kb][hf] + mt * 32 * KT * 2);
-          o[mt] = mfma32(as_bf16x8(vw), pb[kb][hf], o[mt]);
-        }
+      for (int mt = 0; mt < NMT; ++mt) {
+        const u32x2_t lo = ds_read_tr16(sb + v_roff[mt] + (16 * r) * D * 2);
+        const u32x2_t hi = ds_read_tr16(sb + v_roff[mt] + (16 * r + 8) * D * 2);
+        f[mt] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
       }
+    };
+    load(0, vf[0]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (r + 1 < 4) load(r + 1, vf[(r + 1) & 1]);
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) o[mt] = mfma32(as_bf16x8(vf[r & 1][mt]), pb[r >> 1][r & 1], o[mt]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // ---- pipeline: tile t+1 is in flight (K by DMA, V in registers) while tile t computes
-  auto step = [&](int cur, int nxt, int t) {
-    const bool more = t + 1 < ntiles;
-    if (more) issue_tile(nxt, t + 1);
-    compute_tile(cur, t);
-    if (more) store_vt(nxt);
+  // ---- pipeline: the K and V tiles of step t+1 are in flight (DMA into buffer 1-P) while tile
+  // t computes from buffer P; one barrier per tile. Past the last tile the loads repeat the
+  // last tile, so the instruction stream is the same for every step.
+  auto step = [&](int P, int t) {
+    const int tn = t + 1 < ntiles ? t + 1 : ntiles - 1;
+    issue_k(1 - P, tn);
+    issue_v(1 - P, tn);
+    f32x16_t sc[2];
+    s_product(P, sc);
+    mask_tile(sc, t);
+    uint32_t pk[2][8];
+    float ls = probs(sc, pk, false);
+    const float lt = l_run + ls;
+    if (shifted || __any(!(ls <= 0x1p32f) || !(lt + xor_shfl(lt, 32) >= 0x1p-100f))) {
+      rescale(sc);
+      ls = probs(sc, pk, true);
+      shifted = true;
+    }
+    l_run += ls;
+    pv_product(P, pk);
     wait_vmem();
     __syncthreads();
   };
 
-  issue_tile(0, 0);
-  store_vt(0);
+  issue_k(0, 0);
+  issue_v(0, 0);
   wait_vmem();
   __syncthreads();
   int t = 0;
   for (; t + 1 < ntiles; t += 2) {
-    step(0, 1, t);
-    step(1, 0, t + 1);
+    step(0, t);
+    step(1, t + 1);
   }
-  if (t < ntiles) step(0, 1, t);
+  if (t < ntiles) step(0, t);
 
   // ---- epilogue: O / l -> bf16
   const float l_tot = l_run + xor_shfl(l_run, 32);

@@ -113,6 +113,38 @@ def test_peaky_softmax():
     assert n_stable > case.H * 257 // 2
 
 
+@pytest.mark.parametrize("sign", ["neg", "pos", "mixed"])
+def test_extreme_uniform_scores(sign):
+    # Every key row is the same vector x and every query row +-x, all at RoPE position 0, with
+    # gamma = 3.5: every score of a (query head, key) pair is the same value, about +-200 in
+    # log2 units (|s| = gamma^2 sqrt(d) after the RMSNorm). 2^-200 underflows and 2^200
+    # overflows fp32, so the kernel must move its softmax reference (the exact path) to
+    # get anything finite; the exact answer, whatever the rounding, is the running mean of V
+    # (equal scores give uniform weights, D1-2). "mixed" alternates the sign by query head,
+    # so columns of one wave need references 400 log2 units apart.
+    case = W.make_prefill("extreme_" + sign, 31, lengths=[300], H=8, G=2, d=128,
+                          positions=np.zeros(300, np.int32))
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal(case.d).astype(np.float32)
+    sgn = {"neg": -np.ones(case.H), "pos": np.ones(case.H),
+           "mixed": np.where(np.arange(case.H) % 2 == 0, 1.0, -1.0)}[sign].astype(np.float32)
+    q = np.broadcast_to(x[None, None, :] * sgn[None, :, None], (case.N, case.H, case.d))
+    k = np.broadcast_to(x[None, None, :], (case.N, case.G, case.d))
+    case.q = W.encode(np.ascontiguousarray(q), W.BF16)
+    case.k = W.encode(np.ascontiguousarray(k), W.BF16)
+    g = np.full(case.d, 3.5, np.float32)
+    case.q_norm_w = W.encode(g, W.BF16)
+    case.k_norm_w = W.encode(g, W.BF16)
+    say("prefill extreme uniform scores", sign)
+    got = to_f64(run_prefill(case))
+    want = oracle_prefill(case)
+    v = case.f64("v")
+    h = case.H // case.G
+    mean = np.cumsum(v, axis=0) / np.arange(1, case.N + 1)[:, None, None]
+    assert np.allclose(want, np.repeat(mean, h, axis=1), atol=1e-9)  # the closed form
+    check(got, want, W.BF16, "extreme " + sign)
+
+
 def test_default_positions_and_k_out():
     import attention_head_qk_amd as gqa
     case = W.make_prefill("kout", 8, lengths=[70, 33], H=8, G=4, d=128)
