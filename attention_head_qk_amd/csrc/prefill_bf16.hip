@@ -319,7 +319,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   // row sum is taken over the bf16-rounded P that also feeds the P.V product.
   const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
   auto probs = [&](const f32x16_t (&s)[2], uint32_t (&pk)[2][8], bool sub) {
-    float ls = 0.f;
+    float ls4[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: no long dependency chain
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -329,10 +329,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
         f32x2_t pp = {__builtin_amdgcn_exp2f(x0), __builtin_amdgcn_exp2f(x1)};
         const bf16x2_t pb2 = __builtin_convertvector(pp, bf16x2_t);
         pk[kb][j] = __builtin_bit_cast(uint32_t, pb2);
-        ls = __builtin_amdgcn_fdot2_f32_bf16(pb2, one2, ls, false);
+        ls4[j & 3] = __builtin_amdgcn_fdot2_f32_bf16(pb2, one2, ls4[j & 3], false);
       }
     }
-    return ls;
+    return (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
   };
   auto rescale = [&](const f32x16_t (&s)[2]) {
     float mx = fmaxf(s[0][0], s[1][0]);
@@ -391,7 +391,11 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     uint32_t pk[2][8];
     float ls = probs(sc, pk, false);
     const float lt = l_run + ls;
-    if (shifted || __any(!(ls <= 0x1p32f) || !(lt + xor_shfl(lt, 32) >= 0x1p-100f))) {
+    bool exact = shifted || __any(!(ls <= 0x1p32f));
+    // the column sums (lane pairs l, l^32) are only formed when some lane's own sum is small,
+    // which happens on a column's first tiles
+    if (!exact && __any(!(lt >= 0x1p-100f))) exact = __any(!(lt + xor_shfl(lt, 32) >= 0x1p-100f));
+    if (exact) {
       rescale(sc);
       ls = probs(sc, pk, true);
       shifted = true;
