@@ -74,6 +74,21 @@ def test_small_shapes_full(lengths, H, G, d, causal):
     check(got, oracle_prefill(case), W.BF16, case.name)
 
 
+@pytest.mark.parametrize("lengths,H,G,d", [
+    ([1500, 1500], 8, 2, 128),  # dense batch of two, ragged last tile
+    ([1100], 4, 4, 64),         # d = 64, h = 1
+    ([2000], 8, 1, 128),        # h = 8, 125 column blocks of one group
+])
+def test_dense_batches_full(lengths, H, G, d):
+    # mid-size dense causal grids (a few hundred blocks or fewer), every output element
+    case = W.make_prefill(f"dense_{lengths}_{H}_{G}_{d}", 51 + H + G + d, lengths=lengths,
+                          H=H, G=G, d=d)
+    assert case.dense
+    say("prefill", case.name)
+    got = to_f64(run_prefill(case))
+    check(got, oracle_prefill(case), W.BF16, case.name)
+
+
 @pytest.mark.parametrize("lengths,H,G,d,causal", [([150], 16, 8, 64, True), ([70, 0, 33], 12, 4, 128, True),
                                                   ([100], 8, 2, 128, False)])
 def test_small_shapes_f32(lengths, H, G, d, causal):
