@@ -90,3 +90,35 @@ def gqa_prefill(q, k, v, positions, q_norm_w, k_norm_w, eps, theta, causal=True,
     vr = repeat_interleave_heads(v, h)
     sc = scale if scale else 1.0 / math.sqrt(d)
     return mha(qt, kr, vr, causal, sc)
+
+
+def gqa_prefill_cached(q, k, v, k_cache, v_cache, past, q_norm_w, k_norm_w, eps, theta,
+                       scale=None):
+    """One sequence with ``past`` cached tokens (k_cache rows already after the prologue):
+    the new tokens q/k/v [T][.][d] sit at positions past + t; new token t attends to cache
+    rows 0..past-1 and new tokens 0..t, with explicit loops."""
+    T = len(q)
+    H = len(q[0])
+    G = len(k[0])
+    d = len(q[0][0])
+    h = H // G
+    sc = scale if scale else 1.0 / math.sqrt(d)
+    qt = [[prologue_vec(q[t][i], past + t, q_norm_w, eps, theta) for i in range(H)]
+          for t in range(T)]
+    kt = [[prologue_vec(k[t][g], past + t, k_norm_w, eps, theta) for g in range(G)]
+          for t in range(T)]
+    keys = [list(map(list, k_cache[j])) for j in range(past)] + kt
+    vals = [list(map(list, v_cache[j])) for j in range(past)] + [list(map(list, v[t])) for t in range(T)]
+    out = [[[0.0] * d for _ in range(H)] for _ in range(T)]
+    for t in range(T):
+        for i in range(H):
+            g = i // h
+            scores = [sum(qt[t][i][e] * keys[j][g][e] for e in range(d)) * sc
+                      for j in range(past + t + 1)]
+            m = max(scores)
+            ex = [math.exp(x - m) for x in scores]
+            z = sum(ex)
+            for e in range(d):
+                out[t][i][e] = sum(ex[j] / z * vals[j][g][e] for j in range(past + t + 1))
+    return out
+

@@ -220,3 +220,43 @@ def decode_one(q_b, k_rows, v_rows, seq_len, q_norm_w, k_norm_w, eps, theta, pos
         p = attention_weights(qt[i:i + 1], kc[:, g, :], False, scale)[0]
         out[i] = p @ vc[:, g, :]
     return out, k_slot, v_slot
+
+
+# ----------------------------------------------------------------------------- cached prefill
+def prefill_cached(q, k_new, v_new, k_cache, v_cache, cache_lens, cu_seqlens, q_norm_w,
+                   k_norm_w, eps, theta, positions=None, causal=True, scale=None):
+    """Chunked (multi-turn) prefill of new tokens against a KV cache.
+
+    Sequence b has past = cache_lens[b] earlier tokens in the cache: k_cache[b, :past] holds
+    their K after the prologue, v_cache[b, :past] their V (nano-vllm "Qwen3" page, step (6);
+    Qwen3 series 1, D2-3: the cache keeps the K/V of every earlier token). Its new tokens are
+    q/k_new/v_new[cu[b]:cu[b+1]] at positions past + t (or ``positions``). Each layer writes
+    the new tokens' K/V into the cache before attention (D2-3), here at slots past + t, and
+    new token t attends to keys 0 .. past + t (the causal mask of D1-5 with the query at key
+    index past + t). Returns (out [N, H, d], k_cache', v_cache') with the rows appended."""
+    q = np.asarray(q, np.float64)
+    k_new = np.asarray(k_new, np.float64)
+    v_new = np.asarray(v_new, np.float64)
+    kc = np.array(k_cache, dtype=np.float64)
+    vc = np.array(v_cache, dtype=np.float64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    out = np.zeros_like(q)
+    for b in range(len(cu) - 1):
+        s, e = int(cu[b]), int(cu[b + 1])
+        past = int(cache_lens[b])
+        if e == s:
+            continue
+        pos = (past + np.arange(e - s)) if positions is None else np.asarray(positions)[s:e]
+        qt, kt = qk_norm_rope(q[s:e], k_new[s:e], pos, q_norm_w, k_norm_w, eps, theta)
+        kc[b, past:past + e - s] = kt
+        vc[b, past:past + e - s] = v_new[s:e]
+        kv_k = kc[b, :past + e - s]
+        kv_v = vc[b, :past + e - s]
+        H = q.shape[1]
+        h = H // k_new.shape[1]
+        for i in range(H):
+            g = i // h
+            P = attention_weights(qt[:, i, :], kv_k[:, g, :], causal, scale)
+            out[s:e, i, :] = P @ kv_v[:, g, :]
+    return out, kc, vc
+

@@ -399,3 +399,82 @@ def test_peaky_softmax_stays_finite():
         P = O.attention_weights(qt[:r + 1, 0], kt[:r + 1, 0], True)[-1]
         assert P.max() > 0.999
         assert np.allclose(out[r, 0], v[int(np.argmax(P)), 0], atol=1e-2)
+
+
+# ============================================================================ cached prefill
+def _cache_from_prefix(q, k, v, pos, gq, gk, past, max_seq):
+    """Cache rows of a prefix: K after the prologue (as a layer stores it), raw V."""
+    _, kt = O.qk_norm_rope(q[:past], k[:past], pos[:past], gq, gk, 1e-6, 1e6)
+    G, d = k.shape[1], k.shape[2]
+    kc = np.zeros((1, max_seq, G, d))
+    vc = np.zeros((1, max_seq, G, d))
+    kc[0, :past] = kt
+    vc[0, :past] = v[:past]
+    return kc, vc
+
+
+@pytest.mark.parametrize("past,T", [(0, 9), (5, 1), (7, 6), (20, 13)])
+def test_cached_prefill_equals_full_prefill(past, T):
+    # Qwen3 series 1, D2-3: chunked prefill over a cache gives the same attention as one
+    # prefill over the whole sequence (the cache holds what the earlier tokens produced).
+    rng = np.random.default_rng(200 + past + T)
+    L, H, G, d = past + T, 6, 2, 8
+    q, k, v, cu, pos, gq, gk = _case(rng, [L], H=H, G=G, d=d)
+    pos = np.arange(L)
+    full = O.prefill(q, k, v, pos, cu, gq, gk, 1e-6, 1e6)
+    kc, vc = _cache_from_prefix(q, k, v, pos, gq, gk, past, L + 4)
+    out, kc2, vc2 = O.prefill_cached(q[past:], k[past:], v[past:], kc, vc, [past],
+                                     np.array([0, T]), gq, gk, 1e-6, 1e6)
+    assert np.allclose(out, full[past:], atol=1e-12, rtol=0)
+    _, kt = O.qk_norm_rope(q, k, pos, gq, gk, 1e-6, 1e6)
+    assert np.allclose(kc2[0, :L], kt, atol=1e-13) and np.array_equal(vc2[0, :L], v)
+    assert np.array_equal(kc2[0, L:], kc[0, L:])  # rows past the chunk untouched
+
+
+def test_cached_prefill_one_token_is_decode():
+    rng = np.random.default_rng(210)
+    L, H, G, d = 11, 4, 2, 8
+    q, k, v, cu, pos, gq, gk = _case(rng, [L], H=H, G=G, d=d)
+    pos = np.arange(L)
+    kc, vc = _cache_from_prefix(q, k, v, pos, gq, gk, L - 1, L + 2)
+    out, _, _ = O.prefill_cached(q[L - 1:], k[L - 1:], v[L - 1:], kc, vc, [L - 1],
+                                 np.array([0, 1]), gq, gk, 1e-6, 1e6)
+    dec, _, _ = O.decode_one(q[L - 1], kc[0], vc[0], L, gq, gk, 1e-6, 1e6, k_new=k[L - 1],
+                             v_new=v[L - 1])
+    assert np.allclose(out[0], dec, atol=1e-13)
+
+
+def test_cached_prefill_matches_brute_force_and_packs():
+    rng = np.random.default_rng(220)
+    H, G, d = 4, 2, 4
+    pasts, lens = [3, 0, 6], [2, 4, 0]
+    N, max_seq = sum(lens), 12
+    q = rng.standard_normal((N, H, d))
+    k = rng.standard_normal((N, G, d))
+    v = rng.standard_normal((N, G, d))
+    kc = rng.standard_normal((3, max_seq, G, d))  # any cache contents
+    vc = rng.standard_normal((3, max_seq, G, d))
+    gq = rng.uniform(0.5, 1.5, d)
+    gk = rng.uniform(0.5, 1.5, d)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    out, kc2, _ = O.prefill_cached(q, k, v, kc, vc, pasts, cu, gq, gk, 1e-3, 1e4)
+    for b in range(3):
+        s, e = cu[b], cu[b + 1]
+        if e == s:
+            assert np.array_equal(kc2[b], kc[b])
+            continue
+        want = brute.gqa_prefill_cached(q[s:e].tolist(), k[s:e].tolist(), v[s:e].tolist(),
+                                        kc[b].tolist(), vc[b].tolist(), pasts[b], gq.tolist(),
+                                        gk.tolist(), 1e-3, 1e4)
+        assert np.allclose(out[s:e], np.array(want), atol=1e-12, rtol=0)
+
+
+def test_cached_prefill_without_cache_is_prefill():
+    rng = np.random.default_rng(230)
+    q, k, v, cu, pos, gq, gk = _case(rng, [7, 12], H=4, G=4, d=8)
+    pos = np.concatenate([np.arange(7), np.arange(12)])
+    want = O.prefill(q, k, v, pos, cu, gq, gk, 1e-6, 1e6)
+    kc = np.zeros((2, 16, 4, 8))
+    out, _, _ = O.prefill_cached(q, k, v, kc, kc, [0, 0], cu, gq, gk, 1e-6, 1e6)
+    assert np.allclose(out, want, atol=1e-13)
+
