@@ -21,7 +21,7 @@ from ._lib import GqaError  # noqa: F401
 
 _lib.load()  # fail at import, loudly, if the HIP library is not built
 
-__all__ = ["prefill", "decode", "qk_norm_rope", "workspace_bytes", "decode_split_keys",
+__all__ = ["prefill", "prefill_cached", "decode", "qk_norm_rope", "workspace_bytes", "decode_split_keys",
            "GqaError"]
 
 _DTYPES = {torch.float32: _lib.GQA_F32, torch.bfloat16: _lib.GQA_BF16}
@@ -133,6 +133,55 @@ def prefill(q, k, v, positions=None, *, causal=True, q_norm_w=None, k_norm_w=Non
     rc = _lib.load().gqa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(positions), _ptr(out), B, T,
                                  H, G, d, 1 if causal else 0, ctypes.byref(p))
     _lib.check(rc, "gqa_prefill")
+    return out
+
+
+def prefill_cached(q, k, v, k_cache, v_cache, cache_lens, positions=None, *, causal=True,
+                   q_norm_w=None, k_norm_w=None, eps=1e-6, theta=1e6, scale=0.0,
+                   cu_seqlens=None, max_seqlen=None, out=None, stream=None, prof=None):
+    """gqa_prefill_cached (bf16). New tokens of sequences that already have cache_lens[b]
+    (device int32 [B]) tokens in k_cache / v_cache [B, max_seq, G, d]: dense q [B, T, H, d],
+    k/v [B, T, G, d], or packed q [N, H, d], k/v [N, G, d] with cu_seqlens and max_seqlen.
+    Their K (after norm + RoPE) and V are written into the caches at slots cache_lens[b] + t,
+    then every new token attends to its sequence's keys up to its own. Returns out like q."""
+    _dev(q, "q")
+    dtype = q.dtype
+    _dev(k, "k", dtype)
+    _dev(v, "v", dtype)
+    _dev(k_cache, "k_cache", dtype)
+    _dev(v_cache, "v_cache", dtype)
+    _dev(cache_lens, "cache_lens", torch.int32)
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [B, max_seq, G, d]")
+    Bc, S, G, d = k_cache.shape
+    if cu_seqlens is None:
+        if q.dim() != 4:
+            raise ValueError("dense cached prefill takes q [B, T, H, d]")
+        B, T, H, d_q = q.shape
+        if k.shape != (B, T, G, d) or v.shape != k.shape:
+            raise ValueError("k and v must be [B, T, G, d]")
+    else:
+        _dev(cu_seqlens, "cu_seqlens", torch.int32)
+        if q.dim() != 3 or max_seqlen is None:
+            raise ValueError("packed cached prefill takes q [N, H, d] and max_seqlen")
+        N, H, d_q = q.shape
+        B = cu_seqlens.numel() - 1
+        T = int(max_seqlen)
+        if k.shape != (N, G, d) or v.shape != k.shape:
+            raise ValueError("k and v must be [N, G, d]")
+    if d_q != d or Bc != B or cache_lens.numel() != B:
+        raise ValueError("q, caches and cache_lens disagree on B or d")
+    _dev(positions, "positions", torch.int32)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", dtype)
+    p = _params(dtype, q_norm_w, k_norm_w, eps, theta, scale, stream, q.device)
+    p.cu_seqlens = _ptr(cu_seqlens)
+    _prof(p, prof)
+    rc = _lib.load().gqa_prefill_cached(_ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(cache_lens), _ptr(positions), _ptr(out), B, T, H,
+                                        G, d, S, 1 if causal else 0, ctypes.byref(p))
+    _lib.check(rc, "gqa_prefill_cached")
     return out
 
 

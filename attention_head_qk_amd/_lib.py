@@ -43,6 +43,8 @@ class GqaParams(ctypes.Structure):
 SIGNATURES = {
     "gqa_params_init": (None, [ctypes.POINTER(GqaParams)]),
     "gqa_prefill": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, ctypes.POINTER(GqaParams)]),
+    "gqa_prefill_cached": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
+                                ctypes.POINTER(GqaParams)]),
     "gqa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.POINTER(GqaParams)]),
     "gqa_qk_norm_rope": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, ctypes.POINTER(GqaParams)]),
     "gqa_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i, _i, _i]),

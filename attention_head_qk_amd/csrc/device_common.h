@@ -139,11 +139,12 @@ struct PrologueArgs {
   void* v_out;        // decode: V cache
   const int32_t* positions;
   const int32_t* cu_seqlens;  // prefill, packed
-  const int32_t* seq_lens;    // decode
+  const int32_t* seq_lens;    // decode: tokens per sequence; cached prefill: cached rows
   const void* gq;
   const void* gk;
   float eps;
-  int decode;         // 0: token rows (prefill / stand-alone), 1: one row per sequence
+  int decode;         // 0: token rows (prefill / stand-alone), 1: one row per sequence,
+                      // 2: token rows appended to a cache after seq_lens[b] earlier rows
   int B, T, H, G;
   int max_seq;
   int use_rope;
@@ -165,6 +166,9 @@ struct PrefillArgs {
   int causal;
   int n_blk;          // column blocks of the longest sequence
   int zigzag;         // 1: pair heavy and light blocks (see the prefill kernel)
+  const int32_t* cache_lens;  // bf16 kernel, cached prefill: earlier tokens per sequence in
+                              // the cache; kt / v are then caches [B, max_seq, G, D]
+  int max_seq;
   float scale;        // score scale (1/sqrt(d) by default)
   float scale_log2e;  // scale * log2(e)
   double omega[kMaxHalfD];  // bf16 kernel: theta^(-2j/d), computed on the host in fp64

@@ -44,6 +44,7 @@ gqa_status check_params(const gqa_params* p) {
 bool tensor_ok(const void* t) { return t != nullptr && aligned(t, 16); }
 bool opt_tensor_ok(const void* t) { return aligned(t, 16); }
 bool opt_int_ok(const void* t) { return aligned(t, 4); }
+bool int_ok(const void* t) { return t != nullptr && aligned(t, 4); }
 
 float eff_scale(const gqa_params* p, int d) {
   return p->scale > 0.f ? p->scale : (float)(1.0 / std::sqrt((double)d));
@@ -198,6 +199,75 @@ gqa_status gqa_prefill(const void* q, const void* k, const void* v, const int32_
   st = from_hip(bf16 ? gqa::launch_prefill_bf16(fa, d, stream)
                      : gqa::launch_prefill_f32(fa, d, stream));
   if (st != GQA_OK) return st;
+  return from_hip(mark(p->prof_stop, stream));
+}
+
+gqa_status gqa_prefill_cached(const void* q, const void* k, const void* v, void* k_cache,
+                              void* v_cache, const int32_t* cache_lens,
+                              const int32_t* positions, void* out, int B, int T, int H, int G,
+                              int d, int max_seq, int causal, const gqa_params* p) {
+  gqa_status st = check_params(p);
+  if (st != GQA_OK) return st;
+  if ((st = check_heads(H, G, d)) != GQA_OK) return st;
+  if (B < 0 || T < 0 || max_seq < 1 || (causal != 0 && causal != 1)) return GQA_EINVAL;
+  if ((long long)B * T > 0x7fffffffLL) return GQA_EINVAL;
+  if (p->dtype != GQA_BF16) return GQA_ENOTSUP;
+  if ((long long)max_seq * G * d * 2 > 0x7fffffffLL) return GQA_ENOTSUP;
+  if (B == 0 || T == 0) return GQA_OK;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(out) ||
+      !tensor_ok(k_cache) || !tensor_ok(v_cache) || !int_ok(cache_lens))
+    return GQA_EINVAL;
+  if (!opt_int_ok(positions) || !opt_int_ok(p->cu_seqlens)) return GQA_EINVAL;
+
+  hipStream_t stream = reinterpret_cast<hipStream_t>(p->stream);
+  (void)hipGetLastError();
+
+  // K of the new tokens: norm + RoPE at cache_lens[b] + t, written with their V into the caches
+  gqa::PrologueArgs pa{};
+  pa.k = k;
+  pa.v = v;
+  pa.k_out = k_cache;
+  pa.v_out = v_cache;
+  pa.positions = positions;
+  pa.cu_seqlens = p->cu_seqlens;
+  pa.seq_lens = cache_lens;
+  pa.gk = p->k_norm_w;
+  pa.eps = p->eps;
+  pa.decode = 2;
+  pa.B = B;
+  pa.T = T;
+  pa.H = H;
+  pa.G = G;
+  pa.max_seq = max_seq;
+  fill_rope(pa, p, d);
+  if ((st = from_hip(gqa::launch_prologue(pa, B * T, d, true, stream))) != GQA_OK) return st;
+
+  gqa::PrefillArgs fa{};
+  fa.q = q;
+  fa.positions = positions;
+  fa.gq = p->q_norm_w;
+  fa.eps = p->eps;
+  fill_rope(fa, p, d);
+  fa.kt = k_cache;
+  fa.v = v_cache;
+  fa.out = out;
+  fa.cu_seqlens = p->cu_seqlens;
+  fa.cache_lens = cache_lens;
+  fa.max_seq = max_seq;
+  fa.B = B;
+  fa.T = T;
+  fa.H = H;
+  fa.G = G;
+  fa.h = H / G;
+  fa.causal = causal;
+  const long cols = (long)T * fa.h;
+  const int cpb = gqa::prefill_bf16_cols_per_block();
+  fa.n_blk = (int)((cols + cpb - 1) / cpb);
+  fa.zigzag = 0;
+  fa.scale = eff_scale(p, d);
+  fa.scale_log2e = (float)((double)fa.scale * 1.4426950408889634074);
+  if ((st = from_hip(mark(p->prof_start, stream))) != GQA_OK) return st;
+  if ((st = from_hip(gqa::launch_prefill_bf16(fa, d, stream))) != GQA_OK) return st;
   return from_hip(mark(p->prof_stop, stream));
 }
 

@@ -121,9 +121,19 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   const long ncol = (long)Tb * h;
   const long col0 = (long)blk * COLS;
   if (col0 >= ncol) return;
+  // Keys: the sequence's own tokens, or with a cache its past cached rows followed by them
+  // (the query at position p inside the chunk sits at key index past + p). kvrow0 is the
+  // sequence's first K/V row, Tkv its number of keys.
+  int past = 0, Tkv = Tb;
+  long kvrow0 = seq0;
+  if (a.cache_lens) {
+    past = max(0, min(a.cache_lens[b], a.max_seq));
+    kvrow0 = (long)b * a.max_seq;
+    Tkv = min(past + Tb, a.max_seq);
+  }
   const long colmax = (col0 + COLS - 1 < ncol) ? col0 + COLS - 1 : ncol - 1;
   const int p_hi = (int)(colmax / h);
-  const int kv_end = a.causal ? p_hi + 1 : Tb;
+  const int kv_end = a.causal ? min(past + p_hi + 1, Tkv) : Tkv;
   const int ntiles = (kv_end + KT - 1) / KT;
 
   // ---- this lane's column
@@ -133,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   const int head = g * h + (cvalid ? (int)(mycol % h) : 0);
   const long wcol = col0 + wave * 32;
   const int p_wlo = (wcol < ncol) ? (int)(wcol / h) : Tb - 1;  // lowest position in the wave
-  const int plim = a.causal ? pcol : 0x7fffffff;
+  const int plim = a.causal ? past + pcol : 0x7fffffff;
 
   // ---- Q^T (B operand): step st holds d = 16 st + 8 grp + [0, 8) of this lane's column; the
   // rest of the row is in the partner lane l^32. The row is normalised (per-head RMSNorm with
@@ -163,7 +173,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
       ss += xor_shfl(ss, 32);
       rinv = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
     }
-    const int pos = a.positions ? a.positions[seq0 + pcol] : pcol;
+    const int pos = a.positions ? a.positions[seq0 + pcol] : past + pcol;
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
       float x[8];
@@ -190,10 +200,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     }
   }
 
-  // ---- buffer descriptors over this (sequence, group)'s K and V rows; rows >= Tb read as 0
+  // ---- buffer descriptors over this (sequence, group)'s K and V rows; rows >= Tkv read as 0
   const int row_bytes = a.G * D * 2;  // bytes between consecutive tokens
-  const long base_el = ((long)seq0 * a.G + g) * D;
-  const int nrec = (Tb - 1) * row_bytes + D * 2;
+  const long base_el = (kvrow0 * a.G + g) * D;
+  const int nrec = (Tkv - 1) * row_bytes + D * 2;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(reinterpret_cast<const bf16_t*>(a.kt) + base_el, nrec);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(reinterpret_cast<const bf16_t*>(a.v) + base_el, nrec);
 
@@ -295,11 +305,11 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   };
 
   // ---- mask: only tiles that reach past the wave's lowest position, or past the end.
-  // key = t0 + 32 mt + 8 (i/4) + 4 grp + i%4 is visible iff key <= min(plim, Tb - 1).
+  // key = t0 + 32 mt + 8 (i/4) + 4 grp + i%4 is visible iff key <= min(plim, Tkv - 1).
   auto mask_tile = [&](f32x16_t (&s)[2], int t) {
     const int t0 = t * KT;
-    if ((a.causal && t0 + KT - 1 > p_wlo) || t0 + KT > Tb) {
-      const int lim = (plim < Tb - 1 ? plim : Tb - 1) - t0 - 4 * grp;
+    if ((a.causal && t0 + KT - 1 > past + p_wlo) || t0 + KT > Tkv) {
+      const int lim = (plim < Tkv - 1 ? plim : Tkv - 1) - t0 - 4 * grp;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll

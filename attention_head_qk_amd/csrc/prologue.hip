@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(PrologueArgs a) {
   long tok = 0;        // token index of the source rows
   long k_tok_out = 0;  // destination token row for K / V
   int pos = 0;
-  if (!a.decode) {
+  if (a.decode != 1) {
     const int b = slot / a.T, t = slot % a.T;
     active = b < a.B;
     if (active && a.cu_seqlens) {
@@ -65,6 +65,14 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(PrologueArgs a) {
     }
     if (active) pos = a.positions ? a.positions[tok] : t;
     k_tok_out = tok;
+    if (a.decode == 2 && active) {
+      // cached prefill: the token follows the sequence's cached rows; its K/V go to slot
+      // past + t of the cache (rows that would not fit are not written)
+      const int past = max(0, min(a.seq_lens[b], a.max_seq));
+      if (!a.positions) pos = past + t;
+      k_tok_out = (long)b * a.max_seq + past + t;
+      if (r >= nq && past + t >= a.max_seq) active = false;
+    }
   } else {
     active = slot < a.B;
     const int L = active ? a.seq_lens[slot] : 0;

@@ -16,6 +16,9 @@ timed region. Prints one JSON line:
 * roofline: the prefill attention kernel alone (HIP events recorded by the library right
   around its launch, on the launch stream), against the 2.5 PFLOP/s bf16 dense MFMA peak;
   roofline_decode: the decode split-KV kernel alone against 8 TB/s HBM.
+* --workload chunked: gqa_prefill_cached on 4 sequences, each a 2048-token chunk after a
+  cached prefix of U{2048..14336} tokens (H=32, G=8, d=128); FLOPs count every visible
+  (new query, key) pair, cached keys included.
 * cpu_baseline: the fp64 CPU oracle timed on the GPU machine's host on a bounded sample of the
   same prefill workload.
 """
@@ -35,7 +38,7 @@ FP32_PEAK_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
 
 WORKLOADS = ("default", "tiny_f32", "prefill_4k", "varlen", "decode", "long_g4", "long_g1",
-             "copy_calibration")
+             "chunked", "copy_calibration")
 COPY_BYTES = 1 << 30  # bytes read (and written) per step of the copy calibration
 
 
@@ -107,6 +110,32 @@ class Prefill:
                                     out=self.out.view(B, T, c.H, c.d), **kw)
         return self.gqa.prefill(dv["q"], dv["k"], dv["v"], dv["positions"], cu_seqlens=dv["cu"],
                                 max_seqlen=c.T_max, out=self.out, **kw)
+
+    @property
+    def work(self):
+        return self.case.flops
+
+
+class PrefillCached:
+    """gqa_prefill_cached on a chunk workload. Every call appends the same new rows at the
+    same cache slots (cache_lens is not advanced), so repeated calls do identical work."""
+
+    def __init__(self, case):
+        import attention_head_qk_amd as gqa
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from _gpu import device_cached_inputs
+        self.case = case
+        self.dev = device_cached_inputs(case)
+        self.gqa = gqa
+        self.out = self.dev["q"].new_empty(self.dev["q"].shape)
+
+    def __call__(self, prof=None):
+        c, dv = self.case, self.dev
+        return self.gqa.prefill_cached(dv["q"], dv["k"], dv["v"], dv["k_cache"], dv["v_cache"],
+                                       dv["cache_lens"], dv["positions"], causal=c.causal,
+                                       q_norm_w=dv["q_norm_w"], k_norm_w=dv["k_norm_w"],
+                                       eps=c.eps, theta=c.theta, cu_seqlens=dv["cu"],
+                                       max_seqlen=c.T_max, out=self.out, prof=prof)
 
     @property
     def work(self):
@@ -244,7 +273,10 @@ def main(argv=None):
     dev_name = torch.cuda.get_device_name(0)
 
     pre = dec = None
-    if args.workload != "decode":
+    if args.workload == "chunked":
+        pre = PrefillCached(W.prefill_chunked())
+        log(f"bench: cached prefill inputs ready ({pre.case.name}, N={pre.case.N})")
+    elif args.workload != "decode":
         pre = Prefill(prefill_case(args.workload))
         log(f"bench: prefill inputs ready ({pre.case.name}, N={pre.case.N})")
     if args.workload in ("default", "decode"):
@@ -302,6 +334,8 @@ def main(argv=None):
                            "frac_of_peak": round(tf_call / peak, 4)}
         cfg["prefill"] = {"name": c.name, "B": c.B, "lengths_sum": c.N, "T_max": c.T_max, "H": c.H,
                           "G": c.G, "d": c.d, "causal": c.causal, "seed": c.seed}
+        if isinstance(pre, PrefillCached):
+            cfg["prefill"].update(cache_lens=c.cache_lens.tolist(), max_seq=c.max_seq)
     if dec is not None:
         c = dec.case
         call_ms, kern_ms = res["decode"]
@@ -322,7 +356,7 @@ def main(argv=None):
                          "roofline": line.pop("roofline_decode")})
     names = [v["name"] for v in cfg.values()]
     line["config"] = {"workload": " + ".join(names), **cfg}
-    if not args.no_cpu_baseline and pre is not None:
+    if not args.no_cpu_baseline and pre is not None and not isinstance(pre, PrefillCached):
         log("bench: timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline(pre.case)
     elif not args.no_cpu_baseline:

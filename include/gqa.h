@@ -115,6 +115,25 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, const int32_
                        void *out, int B, int T, int H, int G, int d, int causal,
                        const gqa_params *p);
 
+/* Prefill of new tokens against a KV cache (chunked or multi-turn prefill), bf16 only.
+ *   Sequence b has cache_lens[b] earlier tokens in k_cache / v_cache [B, max_seq, G, d] (K
+ *   after norm + RoPE, raw V, as gqa_decode and gqa_prefill's k_out store them).  Its new
+ *   tokens are q [N, H, d], k, v [N, G, d] (raw): dense N = B*T, token b*T + t; or packed
+ *   with p->cu_seqlens as in gqa_prefill.  New token t of sequence b has RoPE position
+ *   cache_lens[b] + t (or positions[token], device [N]).  Its K after the prologue and its V
+ *   are first written into the caches at slot cache_lens[b] + t (zhanghao0806.com page,
+ *   D2-3: the layer writes K/V into the cache before attention; nano-vllm "Qwen3" page,
+ *   step (6)), then with causal = 1 it attends to keys 0 .. cache_lens[b] + t of its sequence
+ *   (D1-5 with the query at key index cache_lens[b] + t); causal = 0: to all
+ *   cache_lens[b] + T_b keys.  out [N, H, d].  cache_lens[b] + T_b <= max_seq is the
+ *   caller's to ensure: rows past max_seq are neither written nor read.  No workspace;
+ *   p->k_out, k_new and v_new are not used.  GQA_ENOTSUP for fp32 and when
+ *   max_seq * G * d * 2 exceeds 2^31 - 1 bytes. */
+gqa_status gqa_prefill_cached(const void *q, const void *k, const void *v, void *k_cache,
+                              void *v_cache, const int32_t *cache_lens,
+                              const int32_t *positions, void *out, int B, int T, int H, int G,
+                              int d, int max_seq, int causal, const gqa_params *p);
+
 /* Single-token decode against a contiguous KV cache.
  *   q [B, H, d] raw query of the new token per sequence; out [B, H, d].
  *   k_cache, v_cache [B, max_seq, G, d]: rows 0..seq_lens[b]-1 are visible to sequence b;

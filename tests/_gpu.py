@@ -143,3 +143,59 @@ def oracle_decode_seq(case: W.DecodeCase, b: int, append=True, position=None):
                         case.eps, case.theta, position=position,
                         k_new=case.f64("k_new")[b] if append else None,
                         v_new=case.f64("v_new")[b] if append else None)
+
+
+def device_cached_inputs(case: W.CachedPrefillCase, fill_invalid=None):
+    """Device tensors for a cached-prefill case: the new tokens (packed) and caches
+    [B, max_seq, G, d] holding cache_lens[b] rows per sequence (the rest zero, or
+    ``fill_invalid``)."""
+    dev = device_prefill_inputs(case.new)
+    shape = (case.B, case.max_seq, case.G, case.d)
+    kc = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+    if fill_invalid is not None:
+        kc.fill_(fill_invalid)
+        vc.fill_(fill_invalid)
+    for b in range(case.B):
+        k, v = case.cache_rows(b)
+        L = k.shape[0]
+        if L:
+            kc[b, :L] = to_dev(k, W.BF16)
+            vc[b, :L] = to_dev(v, W.BF16)
+    dev.update(k_cache=kc, v_cache=vc, cache_lens=i32(case.cache_lens))
+    return dev
+
+
+def run_prefill_cached(case: W.CachedPrefillCase, dev, packed=None, pass_positions=True, **kw):
+    """Run gqa_prefill_cached; packed=None picks dense for one-length batches."""
+    import attention_head_qk_amd as gqa
+    if packed is None:
+        packed = not case.new.dense
+    pos = dev["positions"] if pass_positions else None
+    common = dict(causal=case.causal, q_norm_w=dev["q_norm_w"], k_norm_w=dev["k_norm_w"],
+                  eps=case.eps, theta=case.theta, **kw)
+    args = (dev["k_cache"], dev["v_cache"], dev["cache_lens"], pos)
+    if packed:
+        return gqa.prefill_cached(dev["q"], dev["k"], dev["v"], *args, cu_seqlens=dev["cu"],
+                                  max_seqlen=max(case.T_max, 1), **common)
+    B, T, H, G, d = case.B, case.T_max, case.H, case.G, case.d
+    return gqa.prefill_cached(dev["q"].view(B, T, H, d), dev["k"].view(B, T, G, d),
+                              dev["v"].view(B, T, G, d), *args, **common).view(-1, H, d)
+
+
+def oracle_prefill_cached_seq(case: W.CachedPrefillCase, b: int, positions=None):
+    """Oracle of one sequence: (out [T_b, H, d], K rows [past + T_b, G, d], V rows)."""
+    from oracle import gqa_oracle as O
+    s, e = int(case.cu_seqlens[b]), int(case.cu_seqlens[b + 1])
+    past = int(case.cache_lens[b])
+    k, v = case.cache_rows(b)
+    kc = np.zeros((1, past + e - s, case.G, case.d))
+    vc = np.zeros_like(kc)
+    kc[0, :past] = W.to_f64(k, W.BF16)
+    vc[0, :past] = W.to_f64(v, W.BF16)
+    pos = case.positions[s:e] if positions is None else positions
+    out, kc2, vc2 = O.prefill_cached(case.f64("q")[s:e], case.f64("k")[s:e], case.f64("v")[s:e],
+                                     kc, vc, [past], np.array([0, e - s]), case.f64("q_norm_w"),
+                                     case.f64("k_norm_w"), case.eps, case.theta, positions=pos,
+                                     causal=case.causal)
+    return out, kc2[0], vc2[0]

@@ -25,8 +25,8 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     names = declared_functions()
-    for fn in ("gqa_prefill", "gqa_decode", "gqa_qk_norm_rope", "gqa_workspace_bytes",
-               "gqa_status_str", "gqa_params_init", "gqa_decode_split_keys"):
+    for fn in ("gqa_prefill", "gqa_prefill_cached", "gqa_decode", "gqa_qk_norm_rope",
+               "gqa_workspace_bytes", "gqa_status_str", "gqa_params_init", "gqa_decode_split_keys"):
         assert fn in names
 
 
@@ -119,6 +119,29 @@ def test_prefill_rejects_before_launch(kw, code):
 ])
 def test_decode_rejects_before_launch(kw, code):
     assert _decode(**kw) == code
+
+
+def _prefill_cached(q=A, k=A, v=A, kc=A, vc=A, cl=A, pos=None, out=A, B=2, T=8, H=4, G=2,
+                    d=128, S=64, causal=1, **kw):
+    p = _params(**kw)
+    return _lib.load().gqa_prefill_cached(q, k, v, kc, vc, cl, pos, out, B, T, H, G, d, S, causal,
+                                          ctypes.byref(p))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), _lib.GQA_EINVAL), (dict(k=None), _lib.GQA_EINVAL),
+    (dict(v=MIS), _lib.GQA_EINVAL), (dict(kc=None), _lib.GQA_EINVAL),
+    (dict(vc=MIS), _lib.GQA_EINVAL), (dict(cl=None), _lib.GQA_EINVAL),
+    (dict(cl=A + 2), _lib.GQA_EINVAL), (dict(pos=A + 1), _lib.GQA_EINVAL),
+    (dict(out=None), _lib.GQA_EINVAL), (dict(S=0), _lib.GQA_EINVAL),
+    (dict(causal=3), _lib.GQA_EINVAL), (dict(H=6, G=4), _lib.GQA_EINVAL),
+    (dict(d=96), _lib.GQA_ENOTSUP), (dict(dtype=_lib.GQA_F32), _lib.GQA_ENOTSUP),
+    (dict(S=1 << 20, H=8, G=8), _lib.GQA_ENOTSUP),  # one sequence's cache rows past 2^31 bytes
+    (dict(cu_seqlens=A + 1), _lib.GQA_EINVAL),
+    (dict(B=0), _lib.GQA_OK), (dict(T=0, q=None), _lib.GQA_OK), (dict(B=-1), _lib.GQA_EINVAL),
+])
+def test_prefill_cached_rejects_before_launch(kw, code):
+    assert _prefill_cached(**kw) == code
 
 
 def test_qk_norm_rope_rejects_before_launch():

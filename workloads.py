@@ -14,7 +14,11 @@ post-projection Q/K/V activations at Qwen3 head shapes):
 * Decode draw order from ``default_rng(seed)``: lengths, q, k_new, v_new, gamma_q, gamma_k.
   The cache rows of sequence b come from their own stream ``default_rng([seed, b])`` (K rows
   then V rows), so one sequence can be regenerated on its own.
-* Values are N(0, 1); positions restart at 0 in every packed sequence.
+* Cached prefill: the new tokens are drawn as a prefill case (positions continue from each
+  sequence's cache length); the cache rows of sequence b come from ``default_rng([seed, b])``
+  as for decode. A named workload that draws its cache lengths does so from its own
+  ``default_rng(seed)`` first.
+* Values are N(0, 1); positions restart at 0 in every packed sequence (prefill).
 """
 from __future__ import annotations
 
@@ -236,6 +240,54 @@ def make_decode(name, seed, B=64, len_range=(1024, 32768), max_seq=32768, H=32, 
                       q_norm_w=gq, k_norm_w=gk)
 
 
+# ----------------------------------------------------------------------------- cached prefill
+@dataclasses.dataclass
+class CachedPrefillCase:
+    """New tokens of sequences that already hold ``cache_lens[b]`` tokens in a contiguous
+    cache [B, max_seq, G, d]. ``new`` holds the new tokens packed, at positions
+    cache_lens[b] + t. Cache rows of sequence b come from ``default_rng([seed, b])`` (K rows
+    then V rows), like the decode cache."""
+
+    new: PrefillCase
+    cache_lens: np.ndarray  # int32 [B]
+    max_seq: int
+
+    def __getattr__(self, name):
+        return getattr(self.__dict__["new"], name)
+
+    def cache_rows(self, b: int):
+        """(k_rows, v_rows) of sequence b, each [cache_lens[b], G, d] in storage form."""
+        L = int(self.cache_lens[b])
+        rng = np.random.default_rng([self.new.seed, b])
+        k = encode(_normal(rng, (L, self.new.G, self.new.d)), self.new.dtype)
+        v = encode(_normal(rng, (L, self.new.G, self.new.d)), self.new.dtype)
+        return k, v
+
+    @property
+    def flops(self) -> float:
+        """Algorithmic FLOPs: 4*d*H per visible (query, key) pair; new token t of sequence b
+        sees cache_lens[b] + t + 1 keys (causal) or cache_lens[b] + T_b (not)."""
+        T = self.new.lengths.astype(np.float64)
+        P = self.cache_lens.astype(np.float64)
+        pairs = np.sum(T * P + (T * (T + 1) / 2 if self.new.causal else T * T))
+        return float(4.0 * self.new.d * self.new.H * pairs)
+
+
+def make_cached_prefill(name, seed, lengths, cache_lens, max_seq, H=32, G=8, d=128,
+                        causal=True, gamma="uniform", eps=1e-6, theta=1e6) -> CachedPrefillCase:
+    """New tokens drawn as by ``make_prefill`` (positions cache_lens[b] + t), plus the
+    per-sequence cache streams."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cache_lens = np.asarray(cache_lens, dtype=np.int32)
+    assert lengths.shape == cache_lens.shape
+    assert np.all(cache_lens.astype(np.int64) + lengths <= max_seq)
+    pos = (np.concatenate([c + np.arange(int(t)) for c, t in zip(cache_lens, lengths)])
+           if len(lengths) else np.zeros(0)).astype(np.int32)
+    new = make_prefill(name, seed, lengths=lengths, H=H, G=G, d=d, causal=causal, gamma=gamma,
+                       eps=eps, theta=theta, positions=pos)
+    return CachedPrefillCase(new=new, cache_lens=cache_lens, max_seq=int(max_seq))
+
+
 # ----------------------------------------------------------------------------- named workloads
 def tiny_f32():
     """Tiny fp32 prefill: B=1, T=128, H=16, G=8, d=64, causal, gamma = 1."""
@@ -264,3 +316,12 @@ def prefill_long(G=4):
     seed = 5 if G == 4 else 6
     return make_prefill(f"bf16_prefill_T32768_H64_G{G}_d128", seed, lengths=[32768], H=64,
                         G=G, d=128)
+
+
+def prefill_chunked():
+    """bf16 chunked prefill: 4 sequences, each a 2048-token chunk after a cached prefix of
+    U{2048..14336} tokens, cache of 16384 rows, H=32, G=8, d=128."""
+    rng = np.random.default_rng(7)
+    past = rng.integers(2048, 14336 + 1, size=4)
+    return make_cached_prefill("bf16_chunked_4x2048_after_[2048,14336]_H32_G8_d128", 7,
+                               lengths=[2048] * 4, cache_lens=past, max_seq=16384)
