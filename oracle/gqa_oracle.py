@@ -222,6 +222,34 @@ def decode_one(q_b, k_rows, v_rows, seq_len, q_norm_w, k_norm_w, eps, theta, pos
     return out, k_slot, v_slot
 
 
+# ----------------------------------------------------------------------------- decode loop
+def decode_steps(q_steps, k_steps, v_steps, k_cache, v_cache, cache_lens, q_norm_w, k_norm_w,
+                 eps, theta, scale=None):
+    """S successive decode steps of B sequences: generation is one forward pass per new token,
+    each seeing every earlier token (Qwen3 series 1, D1-1, Q2 and Q5: generate() is many
+    forward() calls; D2-3: each step's K/V join the cache before its attention).
+
+    q_steps [S, B, H, d], k_steps / v_steps [S, B, G, d]: the new token of sequence b at step s
+    (raw). Sequence b starts with cache_lens[b] rows in k_cache / v_cache [B, max_seq, G, d]
+    (K after the prologue, raw V); step s is ``decode_one`` with seq_len cache_lens[b] + s + 1,
+    appending at slot cache_lens[b] + s. Returns (out [S, B, H, d], k_cache', v_cache')."""
+    q_steps = np.asarray(q_steps, np.float64)
+    S, B, H, d = q_steps.shape
+    kc = np.array(k_cache, dtype=np.float64)
+    vc = np.array(v_cache, dtype=np.float64)
+    out = np.zeros((S, B, H, d))
+    for s in range(S):
+        for b in range(B):
+            L = int(cache_lens[b]) + s + 1
+            o, k_slot, v_slot = decode_one(q_steps[s, b], kc[b], vc[b], L, q_norm_w, k_norm_w,
+                                           eps, theta, k_new=k_steps[s][b], v_new=v_steps[s][b],
+                                           scale=scale)
+            out[s, b] = o
+            kc[b, L - 1] = k_slot
+            vc[b, L - 1] = v_slot
+    return out, kc, vc
+
+
 # ----------------------------------------------------------------------------- cached prefill
 def prefill_cached(q, k_new, v_new, k_cache, v_cache, cache_lens, cu_seqlens, q_norm_w,
                    k_norm_w, eps, theta, positions=None, causal=True, scale=None):

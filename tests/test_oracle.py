@@ -478,3 +478,48 @@ def test_cached_prefill_without_cache_is_prefill():
     out, _, _ = O.prefill_cached(q, k, v, kc, kc, [0, 0], cu, gq, gk, 1e-6, 1e6)
     assert np.allclose(out, want, atol=1e-13)
 
+
+
+def test_decode_steps_equal_a_cached_chunk_and_brute_force():
+    # S decode steps with known inputs see exactly what a causal chunk of S new tokens sees
+    # (step s = new token s at slot past + s); checked against prefill_cached and against the
+    # pure-Python brute force, outputs and appended cache rows.
+    rng = np.random.default_rng(240)
+    S, B, H, G, d, max_seq = 5, 3, 6, 2, 8, 16
+    pasts = [0, 4, 9]
+    q = rng.standard_normal((S, B, H, d))
+    k = rng.standard_normal((S, B, G, d))
+    v = rng.standard_normal((S, B, G, d))
+    kc = rng.standard_normal((B, max_seq, G, d))
+    vc = rng.standard_normal((B, max_seq, G, d))
+    gq, gk = rng.uniform(0.5, 1.5, d), rng.uniform(0.5, 1.5, d)
+    out, kc2, vc2 = O.decode_steps(q, k, v, kc, vc, pasts, gq, gk, 1e-6, 1e6)
+    # the chunk view: sequence-major packing of the same tokens
+    qp = q.transpose(1, 0, 2, 3).reshape(B * S, H, d)
+    kp = k.transpose(1, 0, 2, 3).reshape(B * S, G, d)
+    vp = v.transpose(1, 0, 2, 3).reshape(B * S, G, d)
+    cu = np.arange(B + 1) * S
+    ch, kc3, vc3 = O.prefill_cached(qp, kp, vp, kc, vc, pasts, cu, gq, gk, 1e-6, 1e6)
+    assert np.allclose(out.transpose(1, 0, 2, 3).reshape(B * S, H, d), ch, atol=1e-12, rtol=0)
+    assert np.allclose(kc2, kc3, atol=1e-14) and np.array_equal(vc2, vc3)
+    for b in range(B):
+        want = brute.gqa_prefill_cached(q[:, b].tolist(), k[:, b].tolist(), v[:, b].tolist(),
+                                        kc[b].tolist(), vc[b].tolist(), pasts[b], gq.tolist(),
+                                        gk.tolist(), 1e-6, 1e6)
+        assert np.allclose(out[:, b], np.array(want), atol=1e-12, rtol=0)
+        assert np.array_equal(kc2[b, pasts[b] + S:], kc[b, pasts[b] + S:])  # untouched
+
+
+def test_decode_steps_first_token_sees_itself():
+    # An empty sequence's first step has one key, its own: every head returns its V row.
+    rng = np.random.default_rng(250)
+    S, B, H, G, d = 2, 2, 4, 2, 8
+    q = rng.standard_normal((S, B, H, d))
+    k = rng.standard_normal((S, B, G, d))
+    v = rng.standard_normal((S, B, G, d))
+    kc = np.zeros((B, 4, G, d))
+    out, _, vc2 = O.decode_steps(q, k, v, kc, kc.copy(), [0, 0], None, None, 1e-6, 1e6)
+    for b in range(B):
+        for i in range(H):
+            assert np.allclose(out[0, b, i], v[0, b, i // 2], atol=1e-15)
+    assert np.array_equal(vc2[:, :2], v.transpose(1, 0, 2, 3))
