@@ -9,6 +9,7 @@ no fallback when the library is missing (importing raises).
     out = prefill(q, k, v)                       # q [B, T, H, d], k/v [B, T, G, d]
     out = prefill(q, k, v, cu_seqlens=cu, max_seqlen=Tmax)   # packed q [N, H, d]
     out = decode(q, k_cache, v_cache, seq_lens)  # q [B, H, d], caches [B, S, G, d]
+    g = DecodeGraph(q, k_cache, v_cache, seq_lens, k_new, v_new); g.launch()  # per token
 """
 from __future__ import annotations
 
@@ -21,8 +22,8 @@ from ._lib import GqaError  # noqa: F401
 
 _lib.load()  # fail at import, loudly, if the HIP library is not built
 
-__all__ = ["prefill", "prefill_cached", "decode", "qk_norm_rope", "workspace_bytes", "decode_split_keys",
-           "GqaError"]
+__all__ = ["prefill", "prefill_cached", "decode", "DecodeGraph", "qk_norm_rope", "workspace_bytes",
+           "decode_split_keys", "GqaError"]
 
 _DTYPES = {torch.float32: _lib.GQA_F32, torch.bfloat16: _lib.GQA_BF16}
 
@@ -62,8 +63,9 @@ def workspace_bytes(op: str, B: int, T_or_max_seq: int, H: int, G: int, d: int,
     return int(_lib.load().gqa_workspace_bytes(code, B, T_or_max_seq, H, G, d, _DTYPES[dtype]))
 
 
-def decode_split_keys() -> int:
-    return int(_lib.load().gqa_decode_split_keys())
+def decode_split_keys(B: int, H: int, G: int, max_seq: int) -> int:
+    """Keys per split of the decode pass for this decode shape."""
+    return int(_lib.load().gqa_decode_split_keys(B, H, G, max_seq))
 
 
 def _prof(p, prof):
@@ -221,6 +223,84 @@ def decode(q, k_cache, v_cache, seq_lens, *, k_new=None, v_new=None, positions=N
                                 _ptr(out), B, H, G, d, S, ctypes.byref(p))
     _lib.check(rc, "gqa_decode")
     return out
+
+
+class DecodeGraph:
+    """gqa_decode_graph_*: one generation step captured once as a HIP graph.
+
+    Each ``launch()`` first advances seq_lens[b] by one on the device (capped at max_seq), then
+    does what ``decode`` does with k_new / v_new: the new token's K/V are written at slot
+    seq_lens[b] - 1 and its query attends to seq_lens[b] rows; out receives the result. So
+    seq_lens starts at the number of tokens already cached. The tensors are bound at
+    creation: write the next step's q / k_new / v_new into them (in stream order) between
+    launches. The object keeps references to every bound tensor; ``close()`` (or leaving a
+    ``with`` block) waits for the device and releases the graph."""
+
+    def __init__(self, q, k_cache, v_cache, seq_lens, k_new, v_new, *, positions=None,
+                 q_norm_w=None, k_norm_w=None, eps=1e-6, theta=1e6, scale=0.0, out=None,
+                 workspace=None):
+        self._h = None
+        _dev(q, "q")
+        dtype = q.dtype
+        for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (k_new, "k_new"),
+                     (v_new, "v_new")):
+            if t is None:
+                raise ValueError(f"{n} is required")
+            _dev(t, n, dtype)
+        _dev(seq_lens, "seq_lens", torch.int32)
+        _dev(positions, "positions", torch.int32)
+        B, H, d = q.shape
+        _, S, G, d2 = k_cache.shape
+        if d2 != d or v_cache.shape != k_cache.shape or k_cache.shape[0] != B:
+            raise ValueError("caches must be [B, max_seq, G, d]")
+        if k_new.shape != (B, G, d) or v_new.shape != k_new.shape or seq_lens.numel() != B:
+            raise ValueError("k_new / v_new must be [B, G, d] and seq_lens [B]")
+        out = torch.empty_like(q) if out is None else _dev(out, "out", dtype)
+        p = _params(dtype, q_norm_w, k_norm_w, eps, theta, scale, None, q.device)
+        ws = _workspace(workspace, workspace_bytes("decode", B, S, H, G, d, dtype), q.device)
+        p.workspace = _ptr(ws)
+        p.workspace_bytes = ws.numel() * ws.element_size()
+        p.k_new = _ptr(k_new)
+        p.v_new = _ptr(v_new)
+        p.positions = _ptr(positions)
+        self.device = q.device
+        self.out = out
+        self._keep = (q, k_cache, v_cache, seq_lens, k_new, v_new, positions, q_norm_w,
+                      k_norm_w, out, ws)
+        h = ctypes.c_void_p()
+        rc = _lib.load().gqa_decode_graph_create(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                                 _ptr(seq_lens), _ptr(out), B, H, G, d, S,
+                                                 ctypes.byref(p), ctypes.byref(h))
+        _lib.check(rc, "gqa_decode_graph_create")
+        self._h = h
+
+    def launch(self, stream=None):
+        """Enqueue one step on ``stream`` (default: torch's current stream); returns out."""
+        if self._h is None:
+            raise RuntimeError("the decode graph is closed")
+        s = stream if stream is not None else torch.cuda.current_stream(self.device)
+        rc = _lib.load().gqa_decode_graph_launch(self._h, ctypes.c_void_p(s.cuda_stream))
+        _lib.check(rc, "gqa_decode_graph_launch")
+        return self.out
+
+    def close(self):
+        if self._h is not None:
+            torch.cuda.synchronize(self.device)
+            rc = _lib.load().gqa_decode_graph_destroy(self._h)
+            self._h = None
+            _lib.check(rc, "gqa_decode_graph_destroy")
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def qk_norm_rope(q, k=None, positions=None, *, q_norm_w=None, k_norm_w=None, eps=1e-6,

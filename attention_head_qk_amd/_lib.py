@@ -46,9 +46,13 @@ SIGNATURES = {
     "gqa_prefill_cached": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                                 ctypes.POINTER(GqaParams)]),
     "gqa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.POINTER(GqaParams)]),
+    "gqa_decode_graph_create": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                     ctypes.POINTER(GqaParams), ctypes.POINTER(_vp)]),
+    "gqa_decode_graph_launch": (_i, [_vp, _vp]),
+    "gqa_decode_graph_destroy": (_i, [_vp]),
     "gqa_qk_norm_rope": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, ctypes.POINTER(GqaParams)]),
     "gqa_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i, _i, _i]),
-    "gqa_decode_split_keys": (_i, []),
+    "gqa_decode_split_keys": (_i, [_i, _i, _i, _i]),
     "gqa_status_str": (ctypes.c_char_p, [_i]),
 }
 

@@ -6,7 +6,7 @@
 // cache once and does ~4 FLOP per byte, so it is bound by HBM bandwidth (same section: decode
 // is memory-bound, prefill compute-bound).
 //
-// Split pass. A workgroup takes one split of kDecodeSplit keys of one sequence and one KV
+// Split pass. A workgroup takes one split of a.split keys of one sequence and one KV
 // group (and a chunk of HC of the group's h query heads). The K/V cache is token-major
 // [B, max_seq, G, d], so a key row of one group is d contiguous elements: d/8 lanes read it
 // with 16-byte loads, a wave covers 64/(d/8) rows at once and each row-slot of lanes keeps
@@ -90,9 +90,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int g = blockIdx.y / nhc;
   const int head0 = g * a.h + (blockIdx.y % nhc) * HC;
   const int L = a.seq_lens[b];
-  const int k0 = s * kDecodeSplit;
+  const int k0 = s * a.split;
   if (k0 >= L) return;
-  const int k1 = (k0 + kDecodeSplit < L) ? k0 + kDecodeSplit : L;
+  const int k1 = (k0 + a.split < L) ? k0 + a.split : L;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -248,7 +248,6 @@ __global__ __launch_bounds__(256, 2) void decode_split_mfma_kernel(DecodeArgs a)
   constexpr int KSTEP = D / 32;             // k-steps of S^T
   constexpr int NMT = D / 16;               // 16-row tiles of O^T
   constexpr int SUB = 32;                   // keys per step of a wave
-  constexpr int KPW = kDecodeSplit / 4;     // keys per wave
   constexpr int ROWB = D * 2;               // bytes of one staged V row
   constexpr int SUBB = SUB * ROWB;          // one staged V sub-tile
   constexpr int NDMA = SUBB / 1024;         // 1 KB DMA instructions per sub-tile
@@ -271,9 +270,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_mfma_kernel(DecodeArgs a)
   const int g = blockIdx.x / nht;
   const int head0 = (blockIdx.x % nht) * NHEAD;  // first head (inside the group) of this block
   const int L = a.seq_lens[b];
-  const int k0 = s * kDecodeSplit;
+  const int k0 = s * a.split;
   if (k0 >= L) return;
-  const int k1 = (k0 + kDecodeSplit < L) ? k0 + kDecodeSplit : L;
+  const int k1 = (k0 + a.split < L) ? k0 + a.split : L;
+  const int kpw = a.split / 4;  // keys per wave
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -315,8 +315,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_mfma_kernel(DecodeArgs a)
     for (int mt = 0; mt < NMT; ++mt) o[ht][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   char* const vbw[2] = {vb0 + wave * SUBB, vb1 + wave * SUBB};  // this wave's two V buffers
-  const int kw0 = k0 + wave * KPW;
-  const int kw1 = (kw0 + KPW < k1) ? kw0 + KPW : k1;
+  const int kw0 = k0 + wave * kpw;
+  const int kw1 = (kw0 + kpw < k1) ? kw0 + kpw : k1;
   const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
 
   // Loads of one 32-key step: V rows by DMA into buffer `buf` (instruction n fills rows
@@ -491,7 +491,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   const int b = blockIdx.y;
   const int d = threadIdx.x;
   const int L = a.seq_lens[b];
-  const int ns = (L + kDecodeSplit - 1) / kDecodeSplit;
+  const int ns = (L + a.split - 1) / a.split;
   const long base = ((long)b * a.H + head) * a.nsplit;
   T* out = reinterpret_cast<T*>(a.out) + ((long)b * a.H + head) * D + d;
   if (ns == 0) {
@@ -569,6 +569,23 @@ hipError_t launch_decode_split(const DecodeArgs& a, int d, bool bf16, hipStream_
   if (a.B <= 0) return hipSuccess;
   if (bf16) return d == 128 ? split_mfma_d<128>(a, s) : split_mfma_d<64>(a, s);
   return d == 128 ? split_td<float, 128>(a, s) : split_td<float, 64>(a, s);
+}
+
+// One step of a generation loop: every sequence gains the token about to be decoded (its
+// count stops at max_seq).
+__global__ __launch_bounds__(256) void seq_advance_kernel(int32_t* seq_lens, int B, int max_seq) {
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  if (b < B) {
+    const int L = seq_lens[b];
+    seq_lens[b] = L < max_seq ? L + 1 : max_seq;
+  }
+}
+
+hipError_t launch_seq_advance(int32_t* seq_lens, int B, int max_seq, hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(seq_advance_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, s,
+                     seq_lens, B, max_seq);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_combine(const DecodeArgs& a, int d, bool bf16, hipStream_t s) {

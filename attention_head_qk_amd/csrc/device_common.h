@@ -183,10 +183,12 @@ struct DecodeArgs {
   float* part_ml;     // [B, H, nsplit, 2]  (running max in log2 units, sum)
   void* out;          // [B, H, D]
   int B, H, G, h, max_seq, nsplit;
+  int split;          // keys per split, a multiple of 128 (4 waves x 32 keys)
   float scale_log2e;
 };
 
-constexpr int kDecodeSplit = 1024;       // keys per split of the decode pass
+constexpr int kDecodeSplit = 1024;       // longest split of the decode pass (keys)
+constexpr int kDecodeSplitMin = 256;     // shortest split the host picks
 constexpr int kMaxCombineSplits = 4096;  // splits per sequence the combine pass can merge
 
 }  // namespace gqa

@@ -3,6 +3,7 @@
 // a rejected call enqueues nothing and touches no device.
 #include <cmath>
 #include <cstdint>
+#include <new>
 
 #include "gqa.h"
 #include "kernels.h"
@@ -20,8 +21,25 @@ size_t elem_size(int dtype) { return dtype == GQA_BF16 ? 2 : 4; }
 
 bool dtype_ok(int dtype) { return dtype == GQA_F32 || dtype == GQA_BF16; }
 
-int decode_nsplit(int max_seq) {
-  return max_seq <= 0 ? 0 : (max_seq + gqa::kDecodeSplit - 1) / gqa::kDecodeSplit;
+// Keys per split of the decode pass. Splits of 1024 keys stream long caches with few
+// partials; when that would launch fewer than kDecodeMinBlocks workgroups (8 per CU over the
+// longest possible caches) the split is halved, down to kDecodeSplitMin, so that short caches
+// still spread over the chip. Only the host-visible sizes enter (seq_lens live on the device).
+constexpr long kDecodeMinBlocks = 2048;
+
+int decode_split_len(int B, int H, int G, int max_seq) {
+  const long nht = (H / G + 31) / 32;  // head tiles of one group in the bf16 split pass
+  int split = gqa::kDecodeSplit;
+  while (split > gqa::kDecodeSplitMin &&
+         (long)B * G * nht * (((long)max_seq + split - 1) / split) < kDecodeMinBlocks)
+    split /= 2;
+  return split;
+}
+
+int decode_nsplit(int B, int H, int G, int max_seq) {
+  if (max_seq <= 0) return 0;
+  const int split = decode_split_len(B, H, G, max_seq);
+  return (max_seq + split - 1) / split;
 }
 
 // Checks shared by every entry point. Returns GQA_OK or the first failure.
@@ -64,6 +82,90 @@ hipError_t mark(void* ev, hipStream_t s) {
   return ev ? hipEventRecord(reinterpret_cast<hipEvent_t>(ev), s) : hipSuccess;
 }
 
+// Host checks of a decode call (gqa_decode and the decode graph).
+gqa_status decode_check(const void* q, void* k_cache, void* v_cache, const int32_t* seq_lens,
+                        void* out, int B, int H, int G, int d, int max_seq, const gqa_params* p) {
+  gqa_status st = check_params(p);
+  if (st != GQA_OK) return st;
+  if ((st = check_heads(H, G, d)) != GQA_OK) return st;
+  if (B < 0 || max_seq < 0) return GQA_EINVAL;
+  if (B == 0) return GQA_OK;
+  if (max_seq == 0) return GQA_EINVAL;
+  // one sequence's cache rows are addressed with 32-bit byte offsets, and the combine pass
+  // merges at most kMaxCombineSplits splits per sequence
+  if ((long long)max_seq * G * d * (long long)elem_size(p->dtype) > 0x7fffffffLL ||
+      decode_nsplit(B, H, G, max_seq) > gqa::kMaxCombineSplits)
+    return GQA_ENOTSUP;
+  if (!tensor_ok(q) || !tensor_ok(k_cache) || !tensor_ok(v_cache) || !tensor_ok(out))
+    return GQA_EINVAL;
+  if (!seq_lens || !opt_int_ok(seq_lens) || !opt_int_ok(p->positions)) return GQA_EINVAL;
+  if ((p->k_new == nullptr) != (p->v_new == nullptr)) return GQA_EINVAL;
+  if (!opt_tensor_ok(p->k_new) || !opt_tensor_ok(p->v_new)) return GQA_EINVAL;
+  const size_t need = gqa_workspace_bytes(GQA_OP_DECODE, B, max_seq, H, G, d, p->dtype);
+  if (!p->workspace || !aligned(p->workspace, 16) || p->workspace_bytes < need)
+    return GQA_EWORKSPACE;
+  return GQA_OK;
+}
+
+// The decode step's three launches (prologue with the optional append, split pass,
+// combine) on `stream`; `prof` records the caller's events around the split pass.
+gqa_status decode_enqueue(const void* q, void* k_cache, void* v_cache, const int32_t* seq_lens,
+                          void* out, int B, int H, int G, int d, int max_seq,
+                          const gqa_params* p, hipStream_t stream, bool prof) {
+  gqa_status st;
+  const bool bf16 = p->dtype == GQA_BF16;
+  const size_t es = elem_size(p->dtype);
+  const int split = decode_split_len(B, H, G, max_seq);
+  const int ns = decode_nsplit(B, H, G, max_seq);
+  char* ws = static_cast<char*>(p->workspace);
+  void* qt = ws;
+  float* part_o = reinterpret_cast<float*>(ws + align_up((size_t)B * H * d * es));
+  float* part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(part_o) +
+                                            align_up((size_t)B * H * ns * d * 4));
+
+  gqa::PrologueArgs pa{};
+  pa.q = q;
+  pa.k = p->k_new;
+  pa.v = p->v_new;
+  pa.q_out = qt;
+  pa.k_out = k_cache;
+  pa.v_out = v_cache;
+  pa.positions = p->positions;
+  pa.seq_lens = seq_lens;
+  pa.gq = p->q_norm_w;
+  pa.gk = p->k_norm_w;
+  pa.eps = p->eps;
+  pa.decode = 1;
+  pa.B = B;
+  pa.T = 1;
+  pa.H = H;
+  pa.G = G;
+  pa.max_seq = max_seq;
+  fill_rope(pa, p, d);
+  if ((st = from_hip(gqa::launch_prologue(pa, B, d, bf16, stream))) != GQA_OK) return st;
+
+  gqa::DecodeArgs da{};
+  da.qt = qt;
+  da.k_cache = k_cache;
+  da.v_cache = v_cache;
+  da.seq_lens = seq_lens;
+  da.part_o = part_o;
+  da.part_ml = part_ml;
+  da.out = out;
+  da.B = B;
+  da.H = H;
+  da.G = G;
+  da.h = H / G;
+  da.max_seq = max_seq;
+  da.nsplit = ns;
+  da.split = split;
+  da.scale_log2e = (float)((double)eff_scale(p, d) * 1.4426950408889634074);
+  if (prof && (st = from_hip(mark(p->prof_start, stream))) != GQA_OK) return st;
+  if ((st = from_hip(gqa::launch_decode_split(da, d, bf16, stream))) != GQA_OK) return st;
+  if (prof && (st = from_hip(mark(p->prof_stop, stream))) != GQA_OK) return st;
+  return from_hip(gqa::launch_decode_combine(da, d, bf16, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -99,7 +201,10 @@ const char* gqa_status_str(gqa_status s) {
   return "unknown gqa_status";
 }
 
-int gqa_decode_split_keys(void) { return gqa::kDecodeSplit; }
+int gqa_decode_split_keys(int B, int H, int G, int max_seq) {
+  if (B <= 0 || max_seq <= 0 || H <= 0 || G <= 0 || H % G != 0) return 0;
+  return decode_split_len(B, H, G, max_seq);
+}
 
 size_t gqa_workspace_bytes(int op, int B, int T_or_max_seq, int H, int G, int d, int dtype) {
   if (B < 0 || T_or_max_seq < 0 || check_heads(H, G, d) != GQA_OK || !dtype_ok(dtype)) return 0;
@@ -111,7 +216,7 @@ size_t gqa_workspace_bytes(int op, int B, int T_or_max_seq, int H, int G, int d,
     return (dtype == GQA_BF16 ? 0 : align_up(N * H * d * es)) + align_up(N * G * d * es);
   }
   if (op == GQA_OP_DECODE) {
-    const size_t ns = (size_t)decode_nsplit(T_or_max_seq);
+    const size_t ns = (size_t)decode_nsplit(B, H, G, T_or_max_seq);
     return align_up((size_t)B * H * d * es) + align_up((size_t)B * H * ns * d * 4) +
            align_up((size_t)B * H * ns * 2 * 4);
   }
@@ -274,77 +379,70 @@ gqa_status gqa_prefill_cached(const void* q, const void* k, const void* v, void*
 gqa_status gqa_decode(const void* q, void* k_cache, void* v_cache, const int32_t* seq_lens,
                       void* out, int B, int H, int G, int d, int max_seq,
                       const gqa_params* p) {
-  gqa_status st = check_params(p);
-  if (st != GQA_OK) return st;
-  if ((st = check_heads(H, G, d)) != GQA_OK) return st;
-  if (B < 0 || max_seq < 0) return GQA_EINVAL;
-  if (B == 0) return GQA_OK;
-  if (max_seq == 0) return GQA_EINVAL;
-  // one sequence's cache rows are addressed with 32-bit byte offsets, and the combine pass
-  // merges at most kMaxCombineSplits splits per sequence
-  if ((long long)max_seq * G * d * (long long)elem_size(p->dtype) > 0x7fffffffLL ||
-      decode_nsplit(max_seq) > gqa::kMaxCombineSplits)
-    return GQA_ENOTSUP;
-  if (!tensor_ok(q) || !tensor_ok(k_cache) || !tensor_ok(v_cache) || !tensor_ok(out))
-    return GQA_EINVAL;
-  if (!seq_lens || !opt_int_ok(seq_lens) || !opt_int_ok(p->positions)) return GQA_EINVAL;
-  if ((p->k_new == nullptr) != (p->v_new == nullptr)) return GQA_EINVAL;
-  if (!opt_tensor_ok(p->k_new) || !opt_tensor_ok(p->v_new)) return GQA_EINVAL;
-  const size_t need = gqa_workspace_bytes(GQA_OP_DECODE, B, max_seq, H, G, d, p->dtype);
-  if (!p->workspace || !aligned(p->workspace, 16) || p->workspace_bytes < need)
-    return GQA_EWORKSPACE;
+  const gqa_status st = decode_check(q, k_cache, v_cache, seq_lens, out, B, H, G, d, max_seq, p);
+  if (st != GQA_OK || B == 0) return st;
+  (void)hipGetLastError();
+  return decode_enqueue(q, k_cache, v_cache, seq_lens, out, B, H, G, d, max_seq, p,
+                        reinterpret_cast<hipStream_t>(p->stream), true);
+}
 
-  const bool bf16 = p->dtype == GQA_BF16;
-  const size_t es = elem_size(p->dtype);
-  const int ns = decode_nsplit(max_seq);
-  hipStream_t stream = reinterpret_cast<hipStream_t>(p->stream);
-  char* ws = static_cast<char*>(p->workspace);
-  void* qt = ws;
-  float* part_o = reinterpret_cast<float*>(ws + align_up((size_t)B * H * d * es));
-  float* part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(part_o) +
-                                            align_up((size_t)B * H * ns * d * 4));
+// The generation loop's step, captured once: the caller refills q / k_new / v_new between
+// launches, and each launch advances seq_lens on the device before the decode step.
+struct gqa_decode_graph {
+  hipGraphExec_t exec;
+};
+
+gqa_status gqa_decode_graph_create(const void* q, void* k_cache, void* v_cache,
+                                   int32_t* seq_lens, void* out, int B, int H, int G, int d,
+                                   int max_seq, const gqa_params* p, gqa_decode_graph** graph) {
+  if (!graph) return GQA_EINVAL;
+  *graph = nullptr;
+  gqa_status st = decode_check(q, k_cache, v_cache, seq_lens, out, B, H, G, d, max_seq, p);
+  if (st != GQA_OK) return st;
+  if (!p->k_new || !p->v_new) return GQA_EINVAL;  // every step appends its token
   (void)hipGetLastError();
 
-  gqa::PrologueArgs pa{};
-  pa.q = q;
-  pa.k = p->k_new;
-  pa.v = p->v_new;
-  pa.q_out = qt;
-  pa.k_out = k_cache;
-  pa.v_out = v_cache;
-  pa.positions = p->positions;
-  pa.seq_lens = seq_lens;
-  pa.gq = p->q_norm_w;
-  pa.gk = p->k_norm_w;
-  pa.eps = p->eps;
-  pa.decode = 1;
-  pa.B = B;
-  pa.T = 1;
-  pa.H = H;
-  pa.G = G;
-  pa.max_seq = max_seq;
-  fill_rope(pa, p, d);
-  if ((st = from_hip(gqa::launch_prologue(pa, B, d, bf16, stream))) != GQA_OK) return st;
+  hipStream_t cs = nullptr;
+  if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return GQA_EHIP;
+  hipGraph_t g = nullptr;
+  hipGraphExec_t exec = nullptr;
+  if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    (void)hipStreamDestroy(cs);
+    return GQA_EHIP;
+  }
+  st = from_hip(gqa::launch_seq_advance(seq_lens, B, max_seq, cs));
+  if (st == GQA_OK && B > 0)
+    st = decode_enqueue(q, k_cache, v_cache, seq_lens, out, B, H, G, d, max_seq, p, cs, false);
+  // the capture is ended whatever happened inside it
+  const hipError_t ec = hipStreamEndCapture(cs, &g);
+  if (st == GQA_OK && ec != hipSuccess) st = GQA_EHIP;
+  if (st == GQA_OK && hipGraphInstantiate(&exec, g, nullptr, nullptr, 0) != hipSuccess)
+    st = GQA_EHIP;
+  if (g) (void)hipGraphDestroy(g);
+  (void)hipStreamDestroy(cs);
+  if (st != GQA_OK) {
+    if (exec) (void)hipGraphExecDestroy(exec);
+    return st;
+  }
+  gqa_decode_graph* h = new (std::nothrow) gqa_decode_graph{exec};
+  if (!h) {
+    (void)hipGraphExecDestroy(exec);
+    return GQA_EHIP;
+  }
+  *graph = h;
+  return GQA_OK;
+}
 
-  gqa::DecodeArgs da{};
-  da.qt = qt;
-  da.k_cache = k_cache;
-  da.v_cache = v_cache;
-  da.seq_lens = seq_lens;
-  da.part_o = part_o;
-  da.part_ml = part_ml;
-  da.out = out;
-  da.B = B;
-  da.H = H;
-  da.G = G;
-  da.h = H / G;
-  da.max_seq = max_seq;
-  da.nsplit = ns;
-  da.scale_log2e = (float)((double)eff_scale(p, d) * 1.4426950408889634074);
-  if ((st = from_hip(mark(p->prof_start, stream))) != GQA_OK) return st;
-  if ((st = from_hip(gqa::launch_decode_split(da, d, bf16, stream))) != GQA_OK) return st;
-  if ((st = from_hip(mark(p->prof_stop, stream))) != GQA_OK) return st;
-  return from_hip(gqa::launch_decode_combine(da, d, bf16, stream));
+gqa_status gqa_decode_graph_launch(gqa_decode_graph* graph, void* stream) {
+  if (!graph || !graph->exec) return GQA_EINVAL;
+  return from_hip(hipGraphLaunch(graph->exec, reinterpret_cast<hipStream_t>(stream)));
+}
+
+gqa_status gqa_decode_graph_destroy(gqa_decode_graph* graph) {
+  if (!graph) return GQA_OK;
+  const hipError_t e = graph->exec ? hipGraphExecDestroy(graph->exec) : hipSuccess;
+  delete graph;
+  return from_hip(e);
 }
 
 gqa_status gqa_qk_norm_rope(const void* q, const void* k, const int32_t* positions,

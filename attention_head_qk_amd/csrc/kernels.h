@@ -18,5 +18,7 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, int d, hipStream_t s);
 // decode split-KV pass, then the cross-split combine pass.
 hipError_t launch_decode_split(const DecodeArgs& a, int d, bool bf16, hipStream_t s);
 hipError_t launch_decode_combine(const DecodeArgs& a, int d, bool bf16, hipStream_t s);
+// generation loop: seq_lens[b] = min(seq_lens[b] + 1, max_seq) for every b < B.
+hipError_t launch_seq_advance(int32_t* seq_lens, int B, int max_seq, hipStream_t s);
 
 }  // namespace gqa

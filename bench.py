@@ -19,6 +19,10 @@ timed region. Prints one JSON line:
 * --workload chunked: gqa_prefill_cached on 4 sequences, each a 2048-token chunk after a
   cached prefix of U{2048..14336} tokens (H=32, G=8, d=128); FLOPs count every visible
   (new query, key) pair, cached keys included.
+* --workload decode_loop: a generation loop, 16 sequences from cache lengths U{256..2048};
+  each step advances seq_lens on the device and decodes one token per sequence. value = GB/s
+  of the step replayed as one HIP graph (gqa_decode_graph_*); the eager step (a torch add and
+  gqa_decode) is reported beside it.
 * cpu_baseline: the fp64 CPU oracle timed on the GPU machine's host on a bounded sample of the
   same prefill workload.
 """
@@ -38,7 +42,7 @@ FP32_PEAK_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
 
 WORKLOADS = ("default", "tiny_f32", "prefill_4k", "varlen", "decode", "long_g4", "long_g1",
-             "chunked", "copy_calibration")
+             "chunked", "decode_loop", "copy_calibration")
 COPY_BYTES = 1 << 30  # bytes read (and written) per step of the copy calibration
 
 
@@ -249,6 +253,106 @@ def copy_calibration(steps, warmup):
             "ms_per_step": round(ms, 4), "steps": steps, "n_gpus": 1}
 
 
+class DecodeLoop:
+    """A generation loop on the decode-loop workload: every step advances seq_lens by one and
+    decodes one token per sequence (the new K/V appended first). The step's inputs are the
+    workload's first-step tokens, bound once; every 64 steps seq_lens goes back to the
+    starting cache lengths (one 64-byte device copy, inside the timed region), so each block of
+    64 steps repeats the workload's lengths."""
+
+    def __init__(self, case):
+        import attention_head_qk_amd as gqa
+        import torch
+        sys.path.insert(0, os.path.join(ROOT, "tests"))
+        from _gpu import device_steps_inputs
+        self.case = c = case
+        dev = device_steps_inputs(case)
+        self.gqa, self.dev = gqa, dev
+        self.sl0 = dev["seq_lens"]
+        self.kc, self.vc = dev["k_cache"], dev["v_cache"]
+        self.sl = self.sl0.clone()
+        self.q, self.k, self.v = dev["q"][0].clone(), dev["k"][0].clone(), dev["v"][0].clone()
+        self.ws = torch.empty(gqa.workspace_bytes("decode", c.B, c.max_seq, c.H, c.G, c.d),
+                              dtype=torch.uint8, device="cuda")
+        self.out = torch.empty_like(self.q)
+        self.kw = dict(q_norm_w=dev["q_norm_w"], k_norm_w=dev["k_norm_w"], eps=c.eps,
+                       theta=c.theta)
+        self.graph = gqa.DecodeGraph(self.q, self.kc, self.vc, self.sl, self.k, self.v,
+                                     out=self.out, workspace=self.ws, **self.kw)
+
+    def eager(self, i, prof=None):
+        if i % self.case.S == 0:
+            self.sl.copy_(self.sl0)
+        self.sl.add_(1)
+        self.gqa.decode(self.q, self.kc, self.vc, self.sl, k_new=self.k, v_new=self.v,
+                        out=self.out, workspace=self.ws, prof=prof, **self.kw)
+
+    def replay(self, i):
+        if i % self.case.S == 0:
+            self.sl.copy_(self.sl0)
+        self.graph.launch()
+
+    def step_bytes(self, i):
+        """Algorithmic bytes of step i: the K and V rows it sees, plus q in and out."""
+        c = self.case
+        rows = float(c.cache_lens.astype("float64").sum()) + c.B * (i % c.S + 1)
+        return rows * c.G * c.d * 2 * 2 + 2.0 * c.B * c.H * c.d * 2
+
+
+def bench_decode_loop(args, dev_name):
+    import torch
+    import workloads as W
+    loop = DecodeLoop(W.decode_loop())
+    c = loop.case
+    log(f"bench: decode loop inputs ready ({c.name})")
+    K = args.steps
+    nbytes = sum(loop.step_bytes(i) for i in range(K))
+
+    def run(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / K
+
+    graph_ms = run(loop.replay)
+    eager_ms = run(loop.eager)
+    # the split-KV kernel alone, from the library's events around it in eager steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for i, e in enumerate(ev):
+        loop.eager(i, prof=e)
+    torch.cuda.synchronize()
+    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / K
+    gbs = lambda ms: nbytes / K / (ms * 1e-3) / 1e9  # noqa: E731
+    log(f"bench: decode loop graph {graph_ms * 1e3:.2f} us/step, eager {eager_ms * 1e3:.2f} "
+        f"us/step, split kernel {kern_ms * 1e3:.2f} us")
+    line = {"metric": "decode loop GB/s (graph-replayed generation step)",
+            "value": round(gbs(graph_ms), 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+            "warmup": args.warmup, "ms_per_step": round(graph_ms, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "device": dev_name,
+            "graph": {"us_per_step": round(graph_ms * 1e3, 3), "GB/s": round(gbs(graph_ms), 2),
+                      "tokens_per_s": round(c.B / (graph_ms * 1e-3), 1)},
+            "eager": {"us_per_step": round(eager_ms * 1e3, 3), "GB/s": round(gbs(eager_ms), 2),
+                      "tokens_per_s": round(c.B / (eager_ms * 1e-3), 1)},
+            "roofline": {"bound": "hbm", "achieved": round(gbs(kern_ms), 2),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs(kern_ms) / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("decode_split_mfma_kernel", c.name),
+                         "kernel": "decode_split_mfma_kernel", "kernel_ms": round(kern_ms, 5)},
+            "config": {"workload": c.name, "B": c.B, "steps_per_block": c.S,
+                       "cache_lens": c.cache_lens.tolist(), "max_seq": c.max_seq, "H": c.H,
+                       "G": c.G, "d": c.d, "seed": c.seed},
+            "cpu_baseline": None}
+    loop.graph.close()
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -271,6 +375,8 @@ def main(argv=None):
         return 0
     torch.cuda.init()
     dev_name = torch.cuda.get_device_name(0)
+    if args.workload == "decode_loop":
+        return bench_decode_loop(args, dev_name)
 
     pre = dec = None
     if args.workload == "chunked":

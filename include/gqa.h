@@ -31,7 +31,8 @@
  *     Element type is params->dtype (fp32 or bf16) for q, k, v, out, caches, k_new, v_new,
  *     k_out and the two norm weights.  Integer arrays are device int32.
  *   - The caller owns all memory.  The library allocates nothing and keeps no state
- *     between calls, so it is re-entrant.  Work is enqueued on params->stream (a
+ *     between calls, so it is re-entrant; the one exception is the decode graph object
+ *     below, which the caller creates and destroys explicitly.  Work is enqueued on params->stream (a
  *     hipStream_t; NULL = the default stream) and the call returns without waiting.
  *     Buffers must stay valid until that stream work has finished.  Outputs must not
  *     alias inputs.
@@ -41,7 +42,8 @@
  *       GQA_ENOTSUP   d not in {64, 128}, an unknown dtype, a bf16 prefill whose
  *                     T * G * d * 2 exceeds 2^31 - 1 bytes (one sequence's K rows), or a
  *                     decode whose max_seq * G * d * element size exceeds 2^31 - 1 bytes
- *                     or max_seq exceeds 4096 * gqa_decode_split_keys();
+ *                     or max_seq exceeds 4096 splits of
+ *                     gqa_decode_split_keys(B, H, G, max_seq) keys;
  *       GQA_EWORKSPACE workspace smaller than gqa_workspace_bytes() or NULL when needed;
  *       GQA_EHIP      a HIP launch error.
  *     A batch with B == 0 or T == 0 is valid and enqueues nothing.  Device faults show up
@@ -145,6 +147,44 @@ gqa_status gqa_decode(const void *q, void *k_cache, void *v_cache, const int32_t
                       void *out, int B, int H, int G, int d, int max_seq,
                       const gqa_params *p);
 
+/* Generation loop: the decode step captured once as a HIP graph and replayed per token.
+ *   Generation runs one forward pass per new token, each seeing every earlier token
+ *   (zhanghao0806.com page, D1-1, Q2 and Q5); the launches of one step are fixed, so they are
+ *   recorded once (nano-vllm "Qwen3" page, the CUDA graph note beside compute_logits) and
+ *   replayed without per-kernel launch cost.
+ *
+ *   gqa_decode_graph_create takes the arguments of gqa_decode; p->k_new and p->v_new are
+ *   required (every step appends its token).  It records, on a private stream, a step that
+ *     1. sets seq_lens[b] = min(seq_lens[b] + 1, max_seq) for every b (device side), then
+ *     2. does exactly what gqa_decode does with these arguments: norm + RoPE of q and k_new,
+ *        k_new / v_new written at slot seq_lens[b] - 1, attention over seq_lens[b] rows.
+ *   So before the first launch seq_lens[b] counts the tokens already in the cache.  Every
+ *   pointer and size, and every field of *p except stream and the profiling events (which
+ *   are ignored), is fixed at creation; the contents of q, k_new, v_new, positions and
+ *   seq_lens are read at each launch, so the caller writes the next token's q / k_new /
+ *   v_new into the same buffers between launches.  A sequence already at max_seq stays
+ *   there and its next token overwrites slot max_seq - 1.  All buffers, including the
+ *   workspace, must stay valid until the graph is destroyed and its launches have finished.
+ *   Errors: those of gqa_decode, GQA_EINVAL without k_new / v_new or with graph == NULL,
+ *   GQA_EHIP if HIP cannot capture or instantiate; on error *graph is NULL.  The graph
+ *   object holds the instantiated HIP graph (no device memory of the library's own).
+ *   B == 0 gives a graph whose launches do nothing.
+ *
+ *   gqa_decode_graph_launch enqueues one step on `stream` (a hipStream_t; NULL = default).
+ *   Launches on one graph must not overlap (they share the workspace); in one stream they
+ *   never do.
+ *   gqa_decode_graph_destroy releases the graph (NULL is accepted); its launches must have
+ *   finished. */
+typedef struct gqa_decode_graph gqa_decode_graph;
+
+gqa_status gqa_decode_graph_create(const void *q, void *k_cache, void *v_cache,
+                                   int32_t *seq_lens, void *out, int B, int H, int G, int d,
+                                   int max_seq, const gqa_params *p, gqa_decode_graph **graph);
+
+gqa_status gqa_decode_graph_launch(gqa_decode_graph *graph, void *stream);
+
+gqa_status gqa_decode_graph_destroy(gqa_decode_graph *graph);
+
 /* The QK prologue alone (RMSNorm then RoPE), for step-level checks.
  *   q [N, H, d] -> q_out [N, H, d]; k [N, G, d] -> k_out [N, G, d]; positions device [N]
  *   or NULL for 0..N-1.  No workspace. */
@@ -156,8 +196,12 @@ gqa_status gqa_qk_norm_rope(const void *q, const void *k, const int32_t *positio
  * T for prefill and max_seq for decode, dtype a gqa_dtype.  Returns 0 for invalid sizes. */
 size_t gqa_workspace_bytes(int op, int B, int T_or_max_seq, int H, int G, int d, int dtype);
 
-/* Keys per split of the decode pass (the split-KV partition of each sequence). */
-int gqa_decode_split_keys(void);
+/* Keys per split of the decode pass (the split-KV partition of each sequence) for a decode
+ * of B sequences, H query heads, G KV heads and a cache of max_seq rows: 1024, halved (down
+ * to 256) while B * G * ceil(H / G / 32) * ceil(max_seq / split) stays below 2048
+ * workgroups, so that short caches still spread over the chip.  0 for invalid sizes.  The
+ * result does not depend on it beyond rounding (splits merge exactly). */
+int gqa_decode_split_keys(int B, int H, int G, int max_seq);
 
 /* Static text for a status code. */
 const char *gqa_status_str(gqa_status s);

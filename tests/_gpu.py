@@ -199,3 +199,38 @@ def oracle_prefill_cached_seq(case: W.CachedPrefillCase, b: int, positions=None)
                                      case.f64("k_norm_w"), case.eps, case.theta, positions=pos,
                                      causal=case.causal)
     return out, kc2[0], vc2[0]
+
+
+def device_steps_inputs(case: W.DecodeStepsCase, fill_invalid=None):
+    """Device tensors for a decode-loop case: per-step q [S, B, H, d], k / v [S, B, G, d],
+    caches [B, max_seq, G, d] holding cache_lens[b] rows (the rest zero or ``fill_invalid``),
+    and seq_lens = cache_lens."""
+    dt = case.dtype
+    tdt = torch.bfloat16 if dt == W.BF16 else torch.float32
+    shape = (case.B, case.max_seq, case.G, case.d)
+    kc = torch.zeros(shape, dtype=tdt, device="cuda")
+    vc = torch.zeros(shape, dtype=tdt, device="cuda")
+    if fill_invalid is not None:
+        kc.fill_(fill_invalid)
+        vc.fill_(fill_invalid)
+    for b in range(case.B):
+        k, v = case.cache_rows(b)
+        if k.shape[0]:
+            kc[b, :k.shape[0]] = to_dev(k, dt)
+            vc[b, :k.shape[0]] = to_dev(v, dt)
+    return dict(q=to_dev(case.q, dt), k=to_dev(case.k, dt), v=to_dev(case.v, dt), k_cache=kc,
+                v_cache=vc, seq_lens=i32(case.cache_lens), q_norm_w=to_dev(case.q_norm_w, dt),
+                k_norm_w=to_dev(case.k_norm_w, dt))
+
+
+def oracle_decode_steps(case: W.DecodeStepsCase):
+    """Oracle of every step: (out [S, B, H, d], k_cache', v_cache') in float64."""
+    from oracle import gqa_oracle as O
+    kc = np.zeros((case.B, case.max_seq, case.G, case.d))
+    vc = np.zeros_like(kc)
+    for b in range(case.B):
+        k, v = case.cache_rows(b)
+        kc[b, :k.shape[0]] = W.to_f64(k, case.dtype)
+        vc[b, :k.shape[0]] = W.to_f64(v, case.dtype)
+    return O.decode_steps(case.f64("q"), case.f64("k"), case.f64("v"), kc, vc, case.cache_lens,
+                          case.f64("q_norm_w"), case.f64("k_norm_w"), case.eps, case.theta)

@@ -25,7 +25,8 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     names = declared_functions()
-    for fn in ("gqa_prefill", "gqa_prefill_cached", "gqa_decode", "gqa_qk_norm_rope",
+    for fn in ("gqa_prefill", "gqa_prefill_cached", "gqa_decode", "gqa_decode_graph_create",
+               "gqa_decode_graph_launch", "gqa_decode_graph_destroy", "gqa_qk_norm_rope",
                "gqa_workspace_bytes", "gqa_status_str", "gqa_params_init", "gqa_decode_split_keys"):
         assert fn in names
 
@@ -59,13 +60,31 @@ def test_workspace_bytes():
     assert ws(_lib.GQA_OP_PREFILL, 1, 3, 2, 1, 64, _lib.GQA_F32) == 1536 + 768
     assert ws(_lib.GQA_OP_PREFILL, 1, 3, 1, 1, 64, _lib.GQA_BF16) == 512  # 384 -> 512
     # decode: q~ + fp32 partial O + fp32 (m, l) per split
-    S = lib.gqa_decode_split_keys()
+    S = lib.gqa_decode_split_keys(64, 32, 8, 32768)
+    assert S == 1024
     ns = -(-32768 // S)
     want = 64 * 32 * 128 * 2 + 64 * 32 * ns * 128 * 4 + 64 * 32 * ns * 2 * 4
     assert ws(_lib.GQA_OP_DECODE, 64, 32768, 32, 8, 128, _lib.GQA_BF16) == want
     assert ws(_lib.GQA_OP_QK_NORM_ROPE, 4, 4, 4, 4, 128, _lib.GQA_BF16) == 0
     assert ws(_lib.GQA_OP_PREFILL, 1, 8, 6, 4, 128, _lib.GQA_BF16) == 0  # H % G != 0
     assert ws(_lib.GQA_OP_PREFILL, 1, 8, 8, 4, 96, _lib.GQA_BF16) == 0   # d unsupported
+
+
+def test_decode_split_rule():
+    f = _lib.load().gqa_decode_split_keys
+    assert f(64, 32, 8, 32768) == 1024            # 16384 blocks at 1024 keys
+    assert f(16, 32, 8, 16384) == 1024            # exactly 2048 blocks
+    assert f(16, 32, 8, 16383) == 1024
+    assert f(16, 32, 8, 8192) == 512              # 1024 blocks at 1024 keys, 2048 at 512
+    assert f(16, 32, 8, 4096) == 256
+    assert f(13, 32, 8, 3100) == 256              # stops at the shortest split
+    assert f(1, 64, 1, 32768) == 256              # MQA: 2 head tiles of 32
+    assert f(256, 64, 1, 32768) == 1024           # 256 x 2 x 32 blocks
+    assert f(0, 32, 8, 100) == 0 and f(4, 6, 4, 100) == 0 and f(4, 8, 4, 0) == 0
+    ws = _lib.load().gqa_workspace_bytes
+    # the workspace follows the split: 16 splits of 256 keys at max_seq 4096
+    assert ws(_lib.GQA_OP_DECODE, 16, 4096, 32, 8, 128, _lib.GQA_BF16) == (
+        16 * 32 * 128 * 2 + 16 * 32 * 16 * 128 * 4 + 16 * 32 * 16 * 2 * 4)
 
 
 def _params(**kw):
@@ -142,6 +161,37 @@ def _prefill_cached(q=A, k=A, v=A, kc=A, vc=A, cl=A, pos=None, out=A, B=2, T=8, 
 ])
 def test_prefill_cached_rejects_before_launch(kw, code):
     assert _prefill_cached(**kw) == code
+
+
+def _graph_create(q=A, kc=A, vc=A, sl=A, out=A, B=2, H=4, G=2, d=128, S=16, out_handle=True,
+                  **kw):
+    kw.setdefault("k_new", A)
+    kw.setdefault("v_new", A)
+    p = _params(**kw)
+    h = ctypes.c_void_p()
+    rc = _lib.load().gqa_decode_graph_create(q, kc, vc, sl, out, B, H, G, d, S, ctypes.byref(p),
+                                             ctypes.byref(h) if out_handle else None)
+    assert not h.value  # nothing is created on a rejected call
+    return rc
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out_handle=False), _lib.GQA_EINVAL),
+    (dict(k_new=None), _lib.GQA_EINVAL), (dict(v_new=None), _lib.GQA_EINVAL),
+    (dict(k_new=None, v_new=None), _lib.GQA_EINVAL),
+    (dict(q=None), _lib.GQA_EINVAL), (dict(sl=None), _lib.GQA_EINVAL),
+    (dict(S=0), _lib.GQA_EINVAL), (dict(H=5, G=2), _lib.GQA_EINVAL),
+    (dict(d=96), _lib.GQA_ENOTSUP), (dict(workspace_bytes=10), _lib.GQA_EWORKSPACE),
+    (dict(positions=A + 2), _lib.GQA_EINVAL), (dict(B=-1), _lib.GQA_EINVAL),
+])
+def test_decode_graph_create_rejects_before_any_hip_call(kw, code):
+    assert _graph_create(**kw) == code
+
+
+def test_decode_graph_launch_and_destroy_null():
+    lib = _lib.load()
+    assert lib.gqa_decode_graph_launch(None, None) == _lib.GQA_EINVAL
+    assert lib.gqa_decode_graph_destroy(None) == _lib.GQA_OK
 
 
 def test_qk_norm_rope_rejects_before_launch():

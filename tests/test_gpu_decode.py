@@ -28,25 +28,30 @@ def test_decode_64_sequences_sampled():
         assert np.array_equal(to_f64(dev["v_cache"][b, L - 1]), v_slot)
 
 
-def edge_lens():
-    """Lengths around the split-KV partition: empty, tiny, both sides of one and two splits,
-    a quarter split (one wave's share), and a ragged multi-split length."""
-    import attention_head_qk_amd as gqa
-    S = gqa.decode_split_keys()
+def edge_lens(S):
+    """Lengths around a split-KV partition of S keys: empty, tiny, both sides of one and two
+    splits, a quarter split (one wave's share), and a ragged multi-split length."""
     return [0, 1, 2, 31, 33, S // 4 - 1, S // 4 + 1, S - 1, S, S + 1, 2 * S, 2 * S + 37, 3 * S - 5]
 
 
+@pytest.mark.parametrize("max_seq", [3100, 24576])
 @pytest.mark.parametrize("dtype", [W.BF16, W.F32])
 @pytest.mark.parametrize("H,G,d", [(32, 8, 128), (12, 4, 128), (8, 8, 64), (16, 1, 128),
                                    (6, 2, 64), (40, 1, 128)])
-def test_decode_edge_lengths(dtype, H, G, d):
-    EDGE_LENS = edge_lens()
-    case = W.make_decode("edge", 61 + H + G + d, B=len(EDGE_LENS), max_seq=max(EDGE_LENS), H=H,
-                         G=G, d=d, dtype=dtype, seq_lens=EDGE_LENS)
-    say("decode edges", dtype, H, G, d)
+def test_decode_edge_lengths(dtype, H, G, d, max_seq):
+    # the split length follows the shape (1024, 512 and 256 all occur over these cases); the
+    # lengths sit on that split's edges
+    import attention_head_qk_amd as gqa
+    B = 13
+    S = gqa.decode_split_keys(B, H, G, max_seq)
+    lens = edge_lens(S)
+    assert len(lens) == B and max(lens) <= max_seq
+    case = W.make_decode("edge", 61 + H + G + d, B=B, max_seq=max_seq, H=H, G=G, d=d,
+                         dtype=dtype, seq_lens=lens)
+    say("decode edges", dtype, H, G, d, "max_seq", max_seq, "split", S)
     dev = device_decode_inputs(case, fill_invalid=float("nan"))
     out = to_f64(run_decode(case, dev))
-    for b, L in enumerate(EDGE_LENS):
+    for b, L in enumerate(lens):
         if L == 0:
             assert np.array_equal(out[b], np.zeros((H, d))), "empty sequence must give zeros"
             continue

@@ -18,6 +18,8 @@ post-projection Q/K/V activations at Qwen3 head shapes):
   sequence's cache length); the cache rows of sequence b come from ``default_rng([seed, b])``
   as for decode. A named workload that draws its cache lengths does so from its own
   ``default_rng(seed)`` first.
+* Decode loop: q, k, v of every step from ``default_rng(seed)`` (then gamma_q, gamma_k); the
+  starting cache rows per sequence as for decode.
 * Values are N(0, 1); positions restart at 0 in every packed sequence (prefill).
 """
 from __future__ import annotations
@@ -240,6 +242,74 @@ def make_decode(name, seed, B=64, len_range=(1024, 32768), max_seq=32768, H=32, 
                       q_norm_w=gq, k_norm_w=gk)
 
 
+# ----------------------------------------------------------------------------- decode loop
+@dataclasses.dataclass
+class DecodeStepsCase:
+    """S generation steps of B sequences: step s brings one new token per sequence
+    (q [S, B, H, d], k / v [S, B, G, d]); sequence b starts with cache_lens[b] cached rows in a
+    contiguous cache [B, max_seq, G, d], drawn from ``default_rng([seed, b])`` as for decode."""
+
+    name: str
+    seed: int
+    dtype: str
+    cache_lens: np.ndarray  # int32 [B]
+    max_seq: int
+    H: int
+    G: int
+    d: int
+    eps: float
+    theta: float
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    q_norm_w: np.ndarray
+    k_norm_w: np.ndarray
+
+    @property
+    def B(self) -> int:
+        return int(self.cache_lens.shape[0])
+
+    @property
+    def S(self) -> int:
+        return int(self.q.shape[0])
+
+    def f64(self, name: str) -> np.ndarray:
+        return to_f64(getattr(self, name), self.dtype)
+
+    def cache_rows(self, b: int):
+        L = int(self.cache_lens[b])
+        rng = np.random.default_rng([self.seed, b])
+        k = encode(_normal(rng, (L, self.G, self.d)), self.dtype)
+        v = encode(_normal(rng, (L, self.G, self.d)), self.dtype)
+        return k, v
+
+    @property
+    def kv_bytes(self) -> float:
+        """Algorithmic bytes of all S steps: every visible K and V row at each step (step s
+        of sequence b sees cache_lens[b] + s + 1 rows), plus q in and out."""
+        el = 2 if self.dtype == BF16 else 4
+        S = self.S
+        rows = float(np.sum(self.cache_lens.astype(np.float64))) * S + self.B * S * (S + 1) / 2
+        return rows * self.G * self.d * 2 * el + 2.0 * S * self.B * self.H * self.d * el
+
+
+def make_decode_steps(name, seed, cache_lens, S, max_seq, H=32, G=8, d=128, dtype=BF16,
+                      gamma="uniform", eps=1e-6, theta=1e6) -> DecodeStepsCase:
+    """Draw order from ``default_rng(seed)``: q, k, v of all steps, gamma_q, gamma_k."""
+    cache_lens = np.asarray(cache_lens, dtype=np.int32)
+    B = cache_lens.shape[0]
+    assert np.all(cache_lens.astype(np.int64) + S <= max_seq)
+    rng = np.random.default_rng(seed)
+    q = encode(_normal(rng, (S, B, H, d)), dtype)
+    k = encode(_normal(rng, (S, B, G, d)), dtype)
+    v = encode(_normal(rng, (S, B, G, d)), dtype)
+    gq = encode(_gamma(rng, d, gamma), dtype)
+    gk = encode(_gamma(rng, d, gamma), dtype)
+    return DecodeStepsCase(name=name, seed=seed, dtype=dtype, cache_lens=cache_lens,
+                           max_seq=int(max_seq), H=H, G=G, d=d, eps=eps, theta=theta, q=q, k=k,
+                           v=v, q_norm_w=gq, k_norm_w=gk)
+
+
 # ----------------------------------------------------------------------------- cached prefill
 @dataclasses.dataclass
 class CachedPrefillCase:
@@ -325,3 +395,12 @@ def prefill_chunked():
     past = rng.integers(2048, 14336 + 1, size=4)
     return make_cached_prefill("bf16_chunked_4x2048_after_[2048,14336]_H32_G8_d128", 7,
                                lengths=[2048] * 4, cache_lens=past, max_seq=16384)
+
+
+def decode_loop():
+    """bf16 generation loop: 16 sequences x 64 steps, starting cache lengths U{256..2048}
+    (drawn first from ``default_rng(8)``), cache of 4096 rows, H=32, G=8, d=128."""
+    rng = np.random.default_rng(8)
+    lens = rng.integers(256, 2048 + 1, size=16)
+    return make_decode_steps("bf16_decode_loop_16x64_from_[256,2048]_H32_G8_d128", 8, lens, 64,
+                             4096)
