@@ -53,8 +53,9 @@ def repeat_interleave_heads(x, h):
     return [[row[g] for g in range(len(row)) for _ in range(h)] for row in x]
 
 
-def mha(q, k, v, causal, scale):
-    """Plain multi-head attention: q, k, v are [T][H][d] nested lists."""
+def mha(q, k, v, causal, scale, visible=None):
+    """Plain multi-head attention: q, k, v are [T][H][d] nested lists. ``visible(r, c)``,
+    when given, decides alone which key c query r sees."""
     T = len(q)
     H = len(q[0])
     d = len(q[0][0])
@@ -63,7 +64,8 @@ def mha(q, k, v, causal, scale):
         for r in range(T):
             scores = []
             for c in range(T):
-                if causal and c > r:
+                hidden = (not visible(r, c)) if visible else (causal and c > r)
+                if hidden:
                     scores.append(-math.inf)
                 else:
                     scores.append(sum(q[r][i][e] * k[c][i][e] for e in range(d)) * scale)
@@ -75,8 +77,10 @@ def mha(q, k, v, causal, scale):
     return out
 
 
-def gqa_prefill(q, k, v, positions, q_norm_w, k_norm_w, eps, theta, causal=True, scale=None):
-    """One sequence: q [T][H][d], k/v [T][G][d] nested lists of floats."""
+def gqa_prefill(q, k, v, positions, q_norm_w, k_norm_w, eps, theta, causal=True, scale=None,
+                visible=None):
+    """One sequence: q [T][H][d], k/v [T][G][d] nested lists of floats. ``visible(r, c)``
+    replaces the causal test when given."""
     T = len(q)
     H = len(q[0])
     G = len(k[0])
@@ -89,7 +93,7 @@ def gqa_prefill(q, k, v, positions, q_norm_w, k_norm_w, eps, theta, causal=True,
     kr = repeat_interleave_heads(kt, h)
     vr = repeat_interleave_heads(v, h)
     sc = scale if scale else 1.0 / math.sqrt(d)
-    return mha(qt, kr, vr, causal, sc)
+    return mha(qt, kr, vr, causal, sc, visible)
 
 
 def gqa_prefill_cached(q, k, v, k_cache, v_cache, past, q_norm_w, k_norm_w, eps, theta,

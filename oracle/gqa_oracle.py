@@ -98,23 +98,47 @@ def softmax_rows(S: np.ndarray) -> np.ndarray:
     return E / np.sum(E, axis=-1, keepdims=True)
 
 
-def attention_weights(qt_i: np.ndarray, kt_g: np.ndarray, causal: bool, scale=None):
+def visible_keys(Tq: int, Tk: int, causal: bool, window: int = 0, block_mask=None,
+                 block: int = 64) -> np.ndarray:
+    """Boolean [Tq, Tk]: which keys each query row may see. Query row r sits at key index
+    i = r + (Tk - Tq); key index j.
+
+    * causal: j <= i (Qwen3 series 1, D1-5).
+    * window W > 0: also j > i - W, the W most recent keys including itself (zizhi168.cn
+      technical-report summary, §3.1: local attention inside a 512-token window).
+    * block_mask [n_blocks, n_blocks] of bools: also block_mask[i // block, j // block], with
+      the diagonal block always kept so that every row sees itself (same section:
+      block-sparse attention over 64-token blocks)."""
+    i = np.arange(Tq)[:, None] + (Tk - Tq)
+    j = np.arange(Tk)[None, :]
+    vis = np.ones((Tq, Tk), dtype=bool)
+    if causal:
+        vis &= j <= i
+    if window:
+        vis &= j > i - int(window)
+    if block_mask is not None:
+        bm = np.asarray(block_mask, dtype=bool)
+        vis &= bm[i // block, j // block] | (i // block == j // block)
+    return vis
+
+
+def attention_weights(qt_i: np.ndarray, kt_g: np.ndarray, causal: bool, scale=None,
+                      window: int = 0, block_mask=None, block: int = 64):
     """P = softmax(q k^T / sqrt(d) + M) for one query head against its KV head.
 
     Qwen3 series 1, D1-4 (formula softmax(QK^T/sqrt(d_k) + M)); D1-5 (M is -inf where the
-    key index exceeds the query index). qt_i: [Tq, d], kt_g: [Tk, d]; with causal masking
-    query row r sits at key index r + (Tk - Tq)."""
+    key index exceeds the query index). qt_i: [Tq, d], kt_g: [Tk, d]; query row r sits at
+    key index r + (Tk - Tq). M is -inf wherever ``visible_keys`` says False."""
     Tq, d = qt_i.shape
     Tk = kt_g.shape[0]
     S = (qt_i @ kt_g.T) * _scale(d, scale)
-    if causal:
-        r = np.arange(Tq)[:, None] + (Tk - Tq)
-        c = np.arange(Tk)[None, :]
-        S = np.where(c > r, -np.inf, S)
+    if causal or window or block_mask is not None:
+        S = np.where(visible_keys(Tq, Tk, causal, window, block_mask, block), S, -np.inf)
     return softmax_rows(S)
 
 
-def attend(qt: np.ndarray, kt: np.ndarray, v: np.ndarray, causal: bool, scale=None):
+def attend(qt: np.ndarray, kt: np.ndarray, v: np.ndarray, causal: bool, scale=None,
+           window: int = 0, block_mask=None, block: int = 64):
     """Grouped-query attention over one sequence.
 
     qt: [T, H, d]; kt, v: [T, G, d]. Query head i uses KV head g = floor(i / h), h = H / G:
@@ -128,18 +152,20 @@ def attend(qt: np.ndarray, kt: np.ndarray, v: np.ndarray, causal: bool, scale=No
     out = np.empty((T, H, d), dtype=np.float64)
     for i in range(H):
         g = i // h
-        P = attention_weights(qt[:, i, :], kt[:, g, :], causal, scale)
+        P = attention_weights(qt[:, i, :], kt[:, g, :], causal, scale, window, block_mask,
+                              block)
         out[:, i, :] = P @ v[:, g, :]
     return out
 
 
 # ----------------------------------------------------------------------------- prefill
 def prefill(q, k, v, positions, cu_seqlens, q_norm_w, k_norm_w, eps, theta, causal=True,
-            scale=None):
+            scale=None, window=0, block_mask=None, block=64):
     """Packed prefill: prologue on every token, then attention inside each sequence.
 
-    q: [N, H, d]; k, v: [N, G, d]; positions: [N]; cu_seqlens: [B+1] offsets. The causal
-    mask uses the index inside the sequence; positions feed RoPE only."""
+    q: [N, H, d]; k, v: [N, G, d]; positions: [N]; cu_seqlens: [B+1] offsets. The masks
+    (causal, window, block_mask: ``visible_keys``) use the index inside the sequence;
+    positions feed RoPE only. One block_mask serves every sequence."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -148,12 +174,13 @@ def prefill(q, k, v, positions, cu_seqlens, q_norm_w, k_norm_w, eps, theta, caus
     for b in range(len(cu_seqlens) - 1):
         s, e = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
         if e > s:
-            out[s:e] = attend(qt[s:e], kt[s:e], v[s:e], causal, scale)
+            out[s:e] = attend(qt[s:e], kt[s:e], v[s:e], causal, scale, window, block_mask,
+                              block)
     return out
 
 
 def prefill_rows(q, k, v, positions, cu_seqlens, rows, q_norm_w, k_norm_w, eps, theta,
-                 causal=True, scale=None):
+                 causal=True, scale=None, window=0, block_mask=None, block=64):
     """Selected output rows of ``prefill``: rows are packed token indices. Each row is the
     same definition evaluated for that query token alone (its full score row over the
     visible keys of its sequence). Returns [len(rows), H, d]."""
@@ -174,11 +201,11 @@ def prefill_rows(q, k, v, positions, cu_seqlens, rows, q_norm_w, k_norm_w, eps, 
         qt = rope(rms_norm(np.asarray(q[t:t + 1], np.float64), q_norm_w, eps),
                   positions[t:t + 1], theta)[0]
         r = int(t - s)
-        hi = r + 1 if causal else e - s
-        vb = np.asarray(v[s:s + hi], np.float64)
+        vis = visible_keys(e - s, e - s, causal, window, block_mask, block)[r]
+        vb = np.asarray(v[s:e], np.float64)[vis]
         for i in range(H):
             g = i // h
-            p = attention_weights(qt[i:i + 1], kt[:hi, g, :], False, scale)[0]
+            p = attention_weights(qt[i:i + 1], kt[vis, g, :], False, scale)[0]
             out[n, i, :] = p @ vb[:, g, :]
     return out
 
@@ -252,7 +279,8 @@ def decode_steps(q_steps, k_steps, v_steps, k_cache, v_cache, cache_lens, q_norm
 
 # ----------------------------------------------------------------------------- cached prefill
 def prefill_cached(q, k_new, v_new, k_cache, v_cache, cache_lens, cu_seqlens, q_norm_w,
-                   k_norm_w, eps, theta, positions=None, causal=True, scale=None):
+                   k_norm_w, eps, theta, positions=None, causal=True, scale=None, window=0,
+                   block_mask=None, block=64):
     """Chunked (multi-turn) prefill of new tokens against a KV cache.
 
     Sequence b has past = cache_lens[b] earlier tokens in the cache: k_cache[b, :past] holds
@@ -261,7 +289,9 @@ def prefill_cached(q, k_new, v_new, k_cache, v_cache, cache_lens, cu_seqlens, q_
     q/k_new/v_new[cu[b]:cu[b+1]] at positions past + t (or ``positions``). Each layer writes
     the new tokens' K/V into the cache before attention (D2-3), here at slots past + t, and
     new token t attends to keys 0 .. past + t (the causal mask of D1-5 with the query at key
-    index past + t). Returns (out [N, H, d], k_cache', v_cache') with the rows appended."""
+    index past + t). ``window`` and ``block_mask`` (see ``visible_keys``) count key indices
+    over the whole sequence, cache included. Returns (out [N, H, d], k_cache', v_cache') with
+    the rows appended."""
     q = np.asarray(q, np.float64)
     k_new = np.asarray(k_new, np.float64)
     v_new = np.asarray(v_new, np.float64)
@@ -284,7 +314,8 @@ def prefill_cached(q, k_new, v_new, k_cache, v_cache, cache_lens, cu_seqlens, q_
         h = H // k_new.shape[1]
         for i in range(H):
             g = i // h
-            P = attention_weights(qt[:, i, :], kv_k[:, g, :], causal, scale)
+            P = attention_weights(qt[:, i, :], kv_k[:, g, :], causal, scale, window,
+                                  block_mask, block)
             out[s:e, i, :] = P @ kv_v[:, g, :]
     return out, kc, vc
 

@@ -523,3 +523,106 @@ def test_decode_steps_first_token_sees_itself():
         for i in range(H):
             assert np.allclose(out[0, b, i], v[0, b, i // 2], atol=1e-15)
     assert np.array_equal(vc2[:, :2], v.transpose(1, 0, 2, 3))
+
+
+# ----------------------------------------------------------------------------- mask variants
+def _mask_case(rng, T, H=4, G=2, d=8):
+    q, k, v, cu, pos, gq, gk = _case(rng, [T], H=H, G=G, d=d)
+    return q, k, v, cu, np.arange(T), gq, gk
+
+
+@pytest.mark.parametrize("W", [12, 13, 40])
+def test_window_at_least_the_sequence_is_plain_causal(W):
+    rng = np.random.default_rng(300 + W)
+    q, k, v, cu, pos, gq, gk = _mask_case(rng, 12)
+    a = O.prefill(q, k, v, pos, cu, gq, gk, 1e-6, 1e6, window=W)
+    b = O.prefill(q, k, v, pos, cu, gq, gk, 1e-6, 1e6)
+    assert np.array_equal(a, b)
+
+
+def test_window_one_returns_own_value():
+    # one visible key (itself): weight 1 on the token's own V row, for every head
+    rng = np.random.default_rng(310)
+    q, k, v, cu, pos, gq, gk = _mask_case(rng, 9, H=6, G=3)
+    out = O.prefill(q, k, v, pos, cu, gq, gk, 1e-6, 1e6, window=1)
+    assert np.allclose(out, np.repeat(v, 2, axis=1), atol=1e-15)
+
+
+@pytest.mark.parametrize("W", [2, 3, 5])
+def test_window_is_prefill_of_the_window_slice(W):
+    # row t sees exactly tokens t-W+1..t: the last row of a plain causal prefill of that
+    # slice (positions kept), and the brute force with an explicit window test
+    rng = np.random.default_rng(320 + W)
+    T = 11
+    q, k, v, cu, pos, gq, gk = _mask_case(rng, T)
+    out = O.prefill(q, k, v, pos, cu, gq, gk, 1e-6, 1e6, window=W)
+    for t in range(T):
+        lo = max(0, t - W + 1)
+        part = O.prefill(q[lo:t + 1], k[lo:t + 1], v[lo:t + 1], pos[lo:t + 1],
+                         np.array([0, t + 1 - lo]), gq, gk, 1e-6, 1e6)
+        assert np.allclose(out[t], part[-1], atol=1e-12, rtol=0)
+    want = brute.gqa_prefill(q.tolist(), k.tolist(), v.tolist(), list(range(T)), gq.tolist(),
+                             gk.tolist(), 1e-6, 1e6, visible=lambda r, c: r - W < c <= r)
+    assert np.allclose(out, np.array(want), atol=1e-12, rtol=0)
+
+
+def test_block_mask_all_set_is_plain_causal():
+    rng = np.random.default_rng(330)
+    q, k, v, cu, pos, gq, gk = _mask_case(rng, 14)
+    bm = np.ones((4, 4), bool)
+    a = O.prefill(q, k, v, pos, cu, gq, gk, 1e-6, 1e6, block_mask=bm, block=4)
+    b = O.prefill(q, k, v, pos, cu, gq, gk, 1e-6, 1e6)
+    assert np.array_equal(a, b)
+
+
+def test_block_mask_empty_is_blockwise_causal():
+    # nothing set: only the diagonal blocks remain (always kept), so attention restarts at
+    # every block boundary: a packed prefill whose sequences are the blocks, positions kept
+    rng = np.random.default_rng(340)
+    T, blk = 14, 4
+    q, k, v, cu, pos, gq, gk = _mask_case(rng, T)
+    out = O.prefill(q, k, v, pos, cu, gq, gk, 1e-6, 1e6, block_mask=np.zeros((4, 4), bool),
+                    block=blk)
+    cut = np.array([0, 4, 8, 12, 14])
+    want = O.prefill(q, k, v, pos, cut, gq, gk, 1e-6, 1e6)
+    assert np.allclose(out, want, atol=1e-13, rtol=0)
+
+
+def test_block_mask_and_window_match_brute_force():
+    rng = np.random.default_rng(350)
+    T, blk, W = 13, 3, 7
+    q, k, v, cu, pos, gq, gk = _mask_case(rng, T)
+    nb = -(-T // blk)
+    bm = rng.random((nb, nb)) < 0.4
+    for causal, win in ((True, 0), (True, W), (False, 0)):
+        out = O.prefill(q, k, v, pos, cu, gq, gk, 1e-6, 1e6, causal=causal, window=win,
+                        block_mask=bm, block=blk)
+
+        def vis(r, c, causal=causal, win=win):
+            if causal and c > r:
+                return False
+            if win and c <= r - win:
+                return False
+            return bool(bm[r // blk][c // blk]) or r // blk == c // blk
+
+        want = brute.gqa_prefill(q.tolist(), k.tolist(), v.tolist(), list(range(T)),
+                                 gq.tolist(), gk.tolist(), 1e-6, 1e6, visible=vis)
+        assert np.allclose(out, np.array(want), atol=1e-12, rtol=0), (causal, win)
+        rows = [0, 2, 3, 7, 12]
+        got = O.prefill_rows(q, k, v, pos, cu, rows, gq, gk, 1e-6, 1e6, causal=causal,
+                             window=win, block_mask=bm, block=blk)
+        assert np.allclose(got, out[rows], atol=1e-13, rtol=0)
+
+
+def test_masks_in_cached_prefill_count_cache_rows():
+    # the same masks over a cached prefix + chunk equal the one-shot masked prefill's rows
+    rng = np.random.default_rng(360)
+    T, past, blk, W = 15, 6, 4, 5
+    q, k, v, cu, pos, gq, gk = _mask_case(rng, T)
+    bm = rng.random((4, 4)) < 0.5
+    full = O.prefill(q, k, v, pos, cu, gq, gk, 1e-6, 1e6, window=W, block_mask=bm, block=blk)
+    kc, vc = _cache_from_prefix(q, k, v, pos, gq, gk, past, T + 2)
+    out, _, _ = O.prefill_cached(q[past:], k[past:], v[past:], kc, vc, [past],
+                                 np.array([0, T - past]), gq, gk, 1e-6, 1e6, window=W,
+                                 block_mask=bm, block=blk)
+    assert np.allclose(out, full[past:], atol=1e-12, rtol=0)
