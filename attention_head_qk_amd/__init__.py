@@ -23,7 +23,7 @@ from ._lib import GqaError  # noqa: F401
 _lib.load()  # fail at import, loudly, if the HIP library is not built
 
 __all__ = ["prefill", "prefill_cached", "decode", "DecodeGraph", "qk_norm_rope", "workspace_bytes",
-           "decode_split_keys", "GqaError"]
+           "decode_split_keys", "pack_block_mask", "GqaError"]
 
 _DTYPES = {torch.float32: _lib.GQA_F32, torch.bfloat16: _lib.GQA_BF16}
 
@@ -89,15 +89,41 @@ def _workspace(ws, nbytes, device):
     return ws
 
 
+def pack_block_mask(mask):
+    """Bit rows of gqa_params.block_mask from a boolean [query blocks, key blocks] array
+    (host, numpy): word w of row qb holds key blocks 32 w .. 32 w + 31, bit j = block
+    32 w + j. Returns a host int32 array [rows, words]; move it to the device to use it."""
+    import numpy as np
+    m = np.asarray(mask, dtype=bool)
+    rows, cols = m.shape
+    words = max(1, (cols + 31) // 32)
+    padded = np.zeros((rows, words * 32), dtype=np.uint64)
+    padded[:, :cols] = m
+    weights = (np.uint64(1) << np.arange(32, dtype=np.uint64))
+    packed = (padded.reshape(rows, words, 32) * weights).sum(axis=2)
+    return packed.astype(np.uint32).view(np.int32)
+
+
+def _masks(p, window, block_mask):
+    p.window = int(window)
+    if block_mask is not None:
+        _dev(block_mask, "block_mask", torch.int32)
+        if block_mask.dim() != 2:
+            raise ValueError("block_mask must be [rows, words] int32 bit rows")
+        p.block_mask = _ptr(block_mask)
+        p.block_mask_words = block_mask.shape[1]
+
+
 def prefill(q, k, v, positions=None, *, causal=True, q_norm_w=None, k_norm_w=None, eps=1e-6,
             theta=1e6, scale=0.0, cu_seqlens=None, max_seqlen=None, k_out=None, out=None,
-            workspace=None, stream=None, prof=None):
+            workspace=None, stream=None, prof=None, window=0, block_mask=None):
     """gqa_prefill. Dense: q [B, T, H, d], k/v [B, T, G, d]. Packed: q [N, H, d], k/v
     [N, G, d] with cu_seqlens (device int32 [B+1]) and max_seqlen >= every length.
     positions: optional device int32 [N] (RoPE positions; default 0..T_b-1 per sequence).
     k_out: optional [N, G, d] receiving the normalised, rotated K. prof: optional
     (start, stop) torch.cuda.Event pair recorded around the attention kernel alone.
-    Returns out like q."""
+    window: keep only the `window` most recent keys (causal only); block_mask: device int32
+    bit rows over 64-key blocks (``pack_block_mask``). Returns out like q."""
     _dev(q, "q")
     dtype = q.dtype
     _dev(k, "k", dtype)
@@ -131,6 +157,7 @@ def prefill(q, k, v, positions=None, *, causal=True, q_norm_w=None, k_norm_w=Non
     p.workspace_bytes = ws.numel() * ws.element_size()
     p.cu_seqlens = _ptr(cu_seqlens)
     p.k_out = _ptr(k_out)
+    _masks(p, window, block_mask)
     _prof(p, prof)
     rc = _lib.load().gqa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(positions), _ptr(out), B, T,
                                  H, G, d, 1 if causal else 0, ctypes.byref(p))
@@ -140,12 +167,15 @@ def prefill(q, k, v, positions=None, *, causal=True, q_norm_w=None, k_norm_w=Non
 
 def prefill_cached(q, k, v, k_cache, v_cache, cache_lens, positions=None, *, causal=True,
                    q_norm_w=None, k_norm_w=None, eps=1e-6, theta=1e6, scale=0.0,
-                   cu_seqlens=None, max_seqlen=None, out=None, stream=None, prof=None):
+                   cu_seqlens=None, max_seqlen=None, out=None, stream=None, prof=None,
+                   window=0, block_mask=None):
     """gqa_prefill_cached (bf16). New tokens of sequences that already have cache_lens[b]
     (device int32 [B]) tokens in k_cache / v_cache [B, max_seq, G, d]: dense q [B, T, H, d],
     k/v [B, T, G, d], or packed q [N, H, d], k/v [N, G, d] with cu_seqlens and max_seqlen.
     Their K (after norm + RoPE) and V are written into the caches at slots cache_lens[b] + t,
-    then every new token attends to its sequence's keys up to its own. Returns out like q."""
+    then every new token attends to its sequence's keys up to its own. window / block_mask
+    as in ``prefill``, over key indices of the whole sequence (cache first). Returns out
+    like q."""
     _dev(q, "q")
     dtype = q.dtype
     _dev(k, "k", dtype)
@@ -179,6 +209,7 @@ def prefill_cached(q, k, v, k_cache, v_cache, cache_lens, positions=None, *, cau
     _dev(out, "out", dtype)
     p = _params(dtype, q_norm_w, k_norm_w, eps, theta, scale, stream, q.device)
     p.cu_seqlens = _ptr(cu_seqlens)
+    _masks(p, window, block_mask)
     _prof(p, prof)
     rc = _lib.load().gqa_prefill_cached(_ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache),
                                         _ptr(cache_lens), _ptr(positions), _ptr(out), B, T, H,

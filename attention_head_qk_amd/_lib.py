@@ -37,6 +37,9 @@ class GqaParams(ctypes.Structure):
         ("stream", _vp),
         ("prof_start", _vp),
         ("prof_stop", _vp),
+        ("window", ctypes.c_int),
+        ("block_mask", _vp),
+        ("block_mask_words", ctypes.c_int),
     ]
 
 

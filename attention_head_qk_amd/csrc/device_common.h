@@ -169,6 +169,10 @@ struct PrefillArgs {
   const int32_t* cache_lens;  // bf16 kernel, cached prefill: earlier tokens per sequence in
                               // the cache; kt / v are then caches [B, max_seq, G, D]
   int max_seq;
+  int window;         // bf16 kernel: > 0 keeps only keys with index > query index - window
+  const uint32_t* block_mask;  // bf16 kernel: [query block][bm_words] bit rows over 64-key
+                               // blocks (bit j of word w = key block 32 w + j), or null
+  int bm_words;
   float scale;        // score scale (1/sqrt(d) by default)
   float scale_log2e;  // scale * log2(e)
   double omega[kMaxHalfD];  // bf16 kernel: theta^(-2j/d), computed on the host in fp64

@@ -77,6 +77,25 @@ void fill_rope(Args& a, const gqa_params* p, int d) {
 
 gqa_status from_hip(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_EHIP; }
 
+// Mask variants of a prefill whose key indices run over [0, n_keys): window needs the causal
+// mask; the block mask needs whole rows over ceil(n_keys / 64) key blocks; both are bf16 only.
+gqa_status check_masks(const gqa_params* p, int causal, long long n_keys) {
+  if (p->window < 0 || (p->window > 0 && !causal)) return GQA_EINVAL;
+  if (p->block_mask) {
+    if (!aligned(p->block_mask, 4) || p->block_mask_words <= 0) return GQA_EINVAL;
+    if ((long long)p->block_mask_words * 32 * 64 < n_keys) return GQA_EINVAL;
+  }
+  if ((p->window > 0 || p->block_mask) && p->dtype != GQA_BF16) return GQA_ENOTSUP;
+  return GQA_OK;
+}
+
+template <typename Args>
+void fill_masks(Args& a, const gqa_params* p) {
+  a.window = p->window;
+  a.block_mask = p->block_mask;
+  a.bm_words = p->block_mask ? p->block_mask_words : 0;
+}
+
 // Records the caller's optional profiling event on the stream.
 hipError_t mark(void* ev, hipStream_t s) {
   return ev ? hipEventRecord(reinterpret_cast<hipEvent_t>(ev), s) : hipSuccess;
@@ -89,6 +108,7 @@ gqa_status decode_check(const void* q, void* k_cache, void* v_cache, const int32
   if (st != GQA_OK) return st;
   if ((st = check_heads(H, G, d)) != GQA_OK) return st;
   if (B < 0 || max_seq < 0) return GQA_EINVAL;
+  if (p->window != 0 || p->block_mask) return GQA_ENOTSUP;
   if (B == 0) return GQA_OK;
   if (max_seq == 0) return GQA_EINVAL;
   // one sequence's cache rows are addressed with 32-bit byte offsets, and the combine pass
@@ -188,6 +208,9 @@ void gqa_params_init(gqa_params* p) {
   p->stream = nullptr;
   p->prof_start = nullptr;
   p->prof_stop = nullptr;
+  p->window = 0;
+  p->block_mask = nullptr;
+  p->block_mask_words = 0;
 }
 
 const char* gqa_status_str(gqa_status s) {
@@ -233,6 +256,9 @@ gqa_status gqa_prefill(const void* q, const void* k, const void* v, const int32_
   if ((long long)B * T > 0x7fffffffLL) return GQA_EINVAL;
   // the bf16 kernel addresses one sequence's K/V rows of a group with 32-bit buffer offsets
   if (p->dtype == GQA_BF16 && (long long)T * G * d * 2 > 0x7fffffffLL) return GQA_ENOTSUP;
+  // the bf16 kernel numbers a sequence's (position, head) columns with 32-bit integers
+  if (p->dtype == GQA_BF16 && (long long)T * (H / G) > 0x7fffffffLL) return GQA_ENOTSUP;
+  if ((st = check_masks(p, causal, T)) != GQA_OK) return st;
   if (B == 0 || T == 0) return GQA_OK;
   if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(out)) return GQA_EINVAL;
   if (!opt_int_ok(positions) || !opt_int_ok(p->cu_seqlens) || !opt_tensor_ok(p->k_out))
@@ -285,6 +311,7 @@ gqa_status gqa_prefill(const void* q, const void* k, const void* v, const int32_
   fa.G = G;
   fa.h = H / G;
   fa.causal = causal;
+  fill_masks(fa, p);
   const long cols = (long)T * fa.h;
   const int cpb = gqa::prefill_bf16_cols_per_block();
   fa.n_blk = (int)((cols + cpb - 1) / cpb);
@@ -318,6 +345,8 @@ gqa_status gqa_prefill_cached(const void* q, const void* k, const void* v, void*
   if ((long long)B * T > 0x7fffffffLL) return GQA_EINVAL;
   if (p->dtype != GQA_BF16) return GQA_ENOTSUP;
   if ((long long)max_seq * G * d * 2 > 0x7fffffffLL) return GQA_ENOTSUP;
+  if ((long long)T * (H / G) > 0x7fffffffLL) return GQA_ENOTSUP;
+  if ((st = check_masks(p, causal, max_seq)) != GQA_OK) return st;
   if (B == 0 || T == 0) return GQA_OK;
   if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(out) ||
       !tensor_ok(k_cache) || !tensor_ok(v_cache) || !int_ok(cache_lens))
@@ -365,6 +394,7 @@ gqa_status gqa_prefill_cached(const void* q, const void* k, const void* v, void*
   fa.G = G;
   fa.h = H / G;
   fa.causal = causal;
+  fill_masks(fa, p);
   const long cols = (long)T * fa.h;
   const int cpb = gqa::prefill_bf16_cols_per_block();
   fa.n_blk = (int)((cols + cpb - 1) / cpb);

@@ -76,7 +76,9 @@ __device__ __forceinline__ u32x2_t ds_read_tr16(const char* lds) {
 
 }  // namespace
 
-template <int D>
+// MASK: bit 0 = sliding window (a.window), bit 1 = 64-key block layout (a.block_mask).
+// CACHE: keys come from caches after a.cache_lens[b] earlier rows (cached prefill).
+template <int D, int MASK, bool CACHE>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int DCH = D / 8;               // 16-byte chunks per K row
   constexpr int NST = D / 16;              // k-steps of S^T = K Q^T
@@ -118,32 +120,117 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     Tb = a.T;
   }
   const int h = a.h;
-  const long ncol = (long)Tb * h;
-  const long col0 = (long)blk * COLS;
+  // column indices fit in 32 bits (the host keeps T * h below 2^31), so the divisions by h
+  // stay 32-bit
+  const int ncol = Tb * h;
+  const int col0 = blk * COLS;
   if (col0 >= ncol) return;
   // Keys: the sequence's own tokens, or with a cache its past cached rows followed by them
   // (the query at position p inside the chunk sits at key index past + p). kvrow0 is the
   // sequence's first K/V row, Tkv its number of keys.
   int past = 0, Tkv = Tb;
   long kvrow0 = seq0;
-  if (a.cache_lens) {
+  if constexpr (CACHE) {
     past = max(0, min(a.cache_lens[b], a.max_seq));
     kvrow0 = (long)b * a.max_seq;
     Tkv = min(past + Tb, a.max_seq);
   }
-  const long colmax = (col0 + COLS - 1 < ncol) ? col0 + COLS - 1 : ncol - 1;
-  const int p_hi = (int)(colmax / h);
+  const int colmax = (col0 + COLS - 1 < ncol) ? col0 + COLS - 1 : ncol - 1;
+  const int p_hi = (int)((unsigned)colmax / (unsigned)h);
   const int kv_end = a.causal ? min(past + p_hi + 1, Tkv) : Tkv;
   const int ntiles = (kv_end + KT - 1) / KT;
 
   // ---- this lane's column
-  const long mycol = col0 + wave * 32 + l32;
+  const int mycol = col0 + wave * 32 + l32;
   const bool cvalid = mycol < ncol;
-  const int pcol = cvalid ? (int)(mycol / h) : Tb - 1;
-  const int head = g * h + (cvalid ? (int)(mycol % h) : 0);
-  const long wcol = col0 + wave * 32;
-  const int p_wlo = (wcol < ncol) ? (int)(wcol / h) : Tb - 1;  // lowest position in the wave
+  const int pcol = cvalid ? (int)((unsigned)mycol / (unsigned)h) : Tb - 1;
+  const int head = g * h + (cvalid ? mycol - pcol * h : 0);
+  const int wcol = col0 + wave * 32;
+  const int p_wlo = (wcol < ncol) ? (int)((unsigned)wcol / (unsigned)h) : Tb - 1;  // lowest position in the wave
   const int plim = a.causal ? past + pcol : 0x7fffffff;
+
+  // ---- the raw Q row, gamma_q and the RoPE position are loaded before anything else: the Q
+  // row comes from HBM (it is read once), and its latency then overlaps the setup below and
+  // the first K/V tile's loads. Lanes past the last column read row 0 (their results are
+  // never stored); a null gamma or position array is replaced by a valid dummy address.
+  u32x4_t qraw[NST], qgam[NST];
+  int qpos_in;
+  {
+    const long qrow = cvalid ? ((long)(seq0 + pcol) * a.H + head) * D : 0;
+    const bf16_t* qp = reinterpret_cast<const bf16_t*>(a.q) + qrow + 8 * grp;
+    const bf16_t* gp = reinterpret_cast<const bf16_t*>(a.gq ? a.gq : a.q) + 8 * grp;
+    const int32_t* pp = a.positions ? a.positions + seq0 + pcol : reinterpret_cast<const int32_t*>(a.q);
+    qpos_in = *pp;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      qraw[st] = *reinterpret_cast<const u32x4_t*>(qp + 16 * st);
+      qgam[st] = *reinterpret_cast<const u32x4_t*>(gp + 16 * st);
+    }
+  }
+
+  // ---- masks beyond causal (MASK bit 0: sliding window, bit 1: block layout). A key tile is
+  // one 64-key block; tiles that no column of the workgroup sees are never visited.
+  const int p_lo = (int)((unsigned)col0 / (unsigned)h);  // lowest position of the workgroup
+  int t_first = 0;
+  if constexpr ((MASK & 1) != 0) {
+    const int klo = past + p_lo - a.window + 1;  // lowest key any column here sees
+    t_first = klo > 0 ? klo / KT : 0;
+  }
+  // query blocks (64 key indices each) of the workgroup's columns: at most three
+  const int qb_lo = (past + p_lo) / KT, qb_hi = (past + p_hi) / KT;
+  const int nqb = ((CACHE ? a.max_seq : a.T) + KT - 1) / KT;  // rows of block_mask
+  auto bm_word = [&](int qb, int w) -> uint32_t {  // word w of query block qb's row
+    return (qb <= qb_hi && qb < nqb && w < a.bm_words) ? a.block_mask[(long)qb * a.bm_words + w]
+                                                       : 0u;
+  };
+  // visible tiles among [32 w, 32 w + 32) for the workgroup: its rows' bits and diagonals
+  auto tile_bits = [&](int w) -> uint32_t {
+    uint32_t bits = bm_word(qb_lo, w) | bm_word(qb_lo + 1, w) | bm_word(qb_lo + 2, w);
+    for (int qb = qb_lo; qb <= qb_hi; ++qb)
+      if ((qb >> 5) == w) bits |= 1u << (qb & 31);
+    return bits;
+  };
+  auto next_tile = [&](int t) -> int {  // first visible tile after t, or ntiles
+    if constexpr ((MASK & 2) == 0) {
+      return t + 1;
+    } else {
+      int c = t + 1;
+      while (c < ntiles) {
+        const int w = c >> 5;
+        const uint32_t bits = tile_bits(w) & (~0u << (c & 31));
+        if (bits) {
+          c = (w << 5) + __builtin_ctz(bits);
+          break;
+        }
+        c = (w + 1) << 5;
+      }
+      return c < ntiles ? c : ntiles;
+    }
+  };
+  // this column: key index, first key of its window, query block; the wave's highest
+  // window start (tiles below it need the lower-edge mask)
+  const int kq = past + pcol;
+  const int lane_lo = (MASK & 1) ? kq - a.window + 1 : 0;
+  const int qb_c = kq / KT;
+  int wlo_hi = 0;
+  if constexpr ((MASK & 1) != 0) {
+    const int wlast = (wcol + 31 < ncol) ? wcol + 31 : ncol - 1;
+    wlo_hi = past + (int)((unsigned)wlast / (unsigned)h) - a.window + 1;
+  }
+  // does this column see any key of tile t? (same answer for both lanes of the column)
+  auto col_sees = [&](int t) -> bool {
+    const int t0 = t * KT;
+    const int hi = min(min(plim, Tkv - 1), t0 + KT - 1);
+    bool vis = max(t0, lane_lo) <= hi;
+    if constexpr ((MASK & 2) != 0) {
+      const int k = qb_c - qb_lo;  // 0..2
+      const int w = t >> 5;
+      const uint32_t row = k == 0 ? bm_word(qb_lo, w) : (k == 1 ? bm_word(qb_lo + 1, w)
+                                                                : bm_word(qb_lo + 2, w));
+      vis = vis && (((row >> (t & 31)) & 1u) != 0u || qb_c == t);
+    }
+    return vis;
+  };
 
   // ---- Q^T (B operand): step st holds d = 16 st + 8 grp + [0, 8) of this lane's column; the
   // rest of the row is in the partner lane l^32. The row is normalised (per-head RMSNorm with
@@ -151,16 +238,30 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   // as the prologue kernel, without a trip through HBM -- then multiplied by scale * log2(e),
   // so that the scores come out of the matrix cores in log2 units, and rounded to bf16.
   bf16x8_t qf[NST];
-  {
-    const long qrow = ((long)(seq0 + pcol) * a.H + head) * D + 8 * grp;
-    const bf16_t* qp = reinterpret_cast<const bf16_t*>(a.q) + qrow;
-    u32x4_t raw[NST];
-#pragma unroll
-    for (int st = 0; st < NST; ++st) {
-      raw[st] = u32x4_t{0u, 0u, 0u, 0u};
-      if (cvalid) raw[st] = *reinterpret_cast<const u32x4_t*>(qp + 16 * st);
+  // RoPE cos / sin: all h heads of a position share them, so with h >= 4 they are computed
+  // once per (position, pair) into the second LDS buffer, which nothing uses before the
+  // first tile's barrier. Only the masked variants do this: their workgroups visit few
+  // tiles, so the start matters; elsewhere the extra barrier and code cost more than the
+  // trigonometry saved.
+  const int npos = p_hi - p_lo + 1;
+  const bool rope_tab = MASK != 0 && a.use_rope && h >= 4 && npos * (D / 2) * 8 <= BUFBYTES;
+  f32x2_t* const tab = reinterpret_cast<f32x2_t*>(smem1);
+  auto build_rope_table = [&]() {
+    for (int e = tid; e < npos * (D / 2); e += 256) {
+      const int p = p_lo + e / (D / 2), j = e % (D / 2);
+      const int pos = a.positions ? a.positions[seq0 + p] : past + p;
+      float c, sn;
+      rope_cos_sin<true>((double)pos * a.omega[j], c, sn);
+      tab[e] = f32x2_t{c, sn};
     }
-    float rinv = 1.f;
+  };
+  auto make_q = [&]() {  // once the first K/V tile is in flight
+    const u32x4_t (&raw)[NST] = qraw;
+    const u32x4_t (&gr)[NST] = qgam;
+    const int pos = a.positions ? qpos_in : past + pcol;
+    // one factor for the norm and the score scale (RoPE is linear, so scaling before the
+    // rotation is the same as after it)
+    float f = a.scale_log2e;
     if (a.gq) {
       float ss = 0.f;
 #pragma unroll
@@ -171,34 +272,42 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
         for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
       }
       ss += xor_shfl(ss, 32);
-      rinv = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
+      f = a.scale_log2e / sqrtf(ss * (1.0f / D) + a.eps);
     }
-    const int pos = a.positions ? a.positions[seq0 + pcol] : past + pcol;
+    const f32x2_t* trow = tab + (pcol - p_lo) * (D / 2) + 4 * grp;
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
       float x[8];
       unpack8(raw[st], x);
       if (a.gq) {
         float gw[8];
-        load8(reinterpret_cast<const bf16_t*>(a.gq) + 16 * st + 8 * grp, gw);
+        unpack8(gr[st], gw);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = (x[e] * rinv) * gw[e];
+        for (int e = 0; e < 8; ++e) x[e] = (x[e] * f) * gw[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= f;
       }
       if (a.use_rope) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           float c, sn;
-          rope_cos_sin<true>((double)pos * a.omega[8 * st + 4 * grp + m], c, sn);
+          if (rope_tab) {
+            const f32x2_t cs = trow[8 * st + m];
+            c = cs[0];
+            sn = cs[1];
+          } else {
+            rope_cos_sin<true>((double)pos * a.omega[8 * st + 4 * grp + m], c, sn);
+          }
+          // explicit FMAs: every kernel variant rounds the rotation the same way
           const float x0 = x[2 * m], x1 = x[2 * m + 1];
-          x[2 * m] = x0 * c - x1 * sn;
-          x[2 * m + 1] = x0 * sn + x1 * c;
+          x[2 * m] = fmaf(x0, c, -(x1 * sn));
+          x[2 * m + 1] = fmaf(x0, sn, x1 * c);
         }
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] *= a.scale_log2e;
       qf[st] = as_bf16x8(pack8(x));
     }
-  }
+  };
 
   // ---- buffer descriptors over this (sequence, group)'s K and V rows; rows >= Tkv read as 0
   const int row_bytes = a.G * D * 2;  // bytes between consecutive tokens
@@ -308,13 +417,23 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   // key = t0 + 32 mt + 8 (i/4) + 4 grp + i%4 is visible iff key <= min(plim, Tkv - 1).
   auto mask_tile = [&](f32x16_t (&s)[2], int t) {
     const int t0 = t * KT;
-    if ((a.causal && t0 + KT - 1 > past + p_wlo) || t0 + KT > Tkv) {
+    bool need = (a.causal && t0 + KT - 1 > past + p_wlo) || t0 + KT > Tkv;
+    if constexpr ((MASK & 1) != 0) need = need || t0 < wlo_hi;
+    // with several query blocks in the workgroup, a visited tile may be hidden from a column
+    if constexpr ((MASK & 2) != 0) need = need || qb_lo != qb_hi;
+    if (need) {
       const int lim = (plim < Tkv - 1 ? plim : Tkv - 1) - t0 - 4 * grp;
+      int lo = lane_lo - t0 - 4 * grp;  // keys below the window
+      if constexpr ((MASK & 2) != 0) {
+        if (qb_lo != qb_hi && !col_sees(t)) lo = 0x7fffffff;
+      }
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * mt + 8 * (i >> 2) + (i & 3) > lim) s[mt][i] = -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          const int kk = 32 * mt + 8 * (i >> 2) + (i & 3);
+          if (kk > lim || (MASK != 0 && kk < lo)) s[mt][i] = -INFINITY;
+        }
       }
     }
   };
@@ -391,41 +510,82 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   // ---- pipeline: the K and V tiles of step t+1 are in flight (DMA into buffer 1-P) while tile
   // t computes from buffer P; one barrier per tile. Past the last tile the loads repeat the
   // last tile, so the instruction stream is the same for every step.
-  auto step = [&](int P, int t) {
-    const int tn = t + 1 < ntiles ? t + 1 : ntiles - 1;
+  // With masks beyond causal a column may have seen no key yet: its sum is then exactly 0
+  // without any underflow, so only columns that have started count for the exact-path test,
+  // and a wave none of whose columns sees the tile skips it (it still takes part in the
+  // loads and the barrier).
+  bool started = MASK == 0;
+  auto step = [&](int P, int t, int tn) {
     issue_k(1 - P, tn);
     issue_v(1 - P, tn);
-    f32x16_t sc[2];
-    s_product(P, sc);
-    mask_tile(sc, t);
-    uint32_t pk[2][8];
-    float ls = probs(sc, pk, false);
-    const float lt = l_run + ls;
-    bool exact = shifted || __any(!(ls <= 0x1p32f));
-    // the column sums (lane pairs l, l^32) are only formed when some lane's own sum is small,
-    // which happens on a column's first tiles
-    if (!exact && __any(!(lt >= 0x1p-100f))) exact = __any(!(lt + xor_shfl(lt, 32) >= 0x1p-100f));
-    if (exact) {
-      rescale(sc);
-      ls = probs(sc, pk, true);
-      shifted = true;
+    bool wave_on = true;
+    if constexpr (MASK != 0) {
+      const bool sees = col_sees(t);
+      started = started || sees;
+      wave_on = __any(sees);
     }
-    l_run += ls;
-    pv_product(P, pk);
+    if (wave_on) {
+      f32x16_t sc[2];
+      s_product(P, sc);
+      mask_tile(sc, t);
+      uint32_t pk[2][8];
+      float ls = probs(sc, pk, false);
+      const float lt = l_run + ls;
+      bool exact = shifted || __any(!(ls <= 0x1p32f));
+      // the column sums (lane pairs l, l^32) are only formed when some lane's own sum is
+      // small, which happens on a column's first tiles
+      if (!exact && __any(started && !(lt >= 0x1p-100f)))
+        exact = __any(started && !(lt + xor_shfl(lt, 32) >= 0x1p-100f));
+      if (exact) {
+        rescale(sc);
+        ls = probs(sc, pk, true);
+        shifted = true;
+      }
+      l_run += ls;
+      pv_product(P, pk);
+    }
     wait_vmem();
     __syncthreads();
   };
 
-  issue_k(0, 0);
-  issue_v(0, 0);
-  wait_vmem();
-  __syncthreads();
-  int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
-    step(0, t);
-    step(1, t + 1);
+  if constexpr (MASK == 0) {
+    issue_k(0, 0);
+    issue_v(0, 0);
+    if (rope_tab) {
+      build_rope_table();
+      __syncthreads();
+    }
+    make_q();
+    wait_vmem();
+    __syncthreads();
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+      step(0, t, t + 1);
+      step(1, t + 1, t + 2 < ntiles ? t + 2 : t + 1);
+    }
+    if (t < ntiles) step(0, t, t);
+  } else {
+    // visible tiles only; past the last one the loads repeat it (same instruction stream)
+    int t = (MASK & 2) ? next_tile(t_first - 1) : t_first;
+    issue_k(0, t);
+    issue_v(0, t);
+    if (rope_tab) {
+      build_rope_table();
+      __syncthreads();
+    }
+    make_q();
+    wait_vmem();
+    __syncthreads();
+    while (true) {
+      const int t1 = next_tile(t);
+      step(0, t, t1 < ntiles ? t1 : t);
+      if (t1 >= ntiles) break;
+      const int t2 = next_tile(t1);
+      step(1, t1, t2 < ntiles ? t2 : t1);
+      if (t2 >= ntiles) break;
+      t = t2;
+    }
   }
-  if (t < ntiles) step(0, t);
 
   // ---- epilogue: O / l -> bf16
   const float l_tot = l_run + xor_shfl(l_run, 32);
@@ -445,16 +605,33 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   }
 }
 
-template <int D>
+template <int D, int MASK, bool CACHE>
 static hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
   const long grid = (long)a.B * a.G * a.n_blk;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D>), dim3((unsigned)grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, MASK, CACHE>), dim3((unsigned)grid), dim3(256), 0,
+                     s, a);
   return hipGetLastError();
+}
+
+template <int D, bool CACHE>
+static hipError_t launch_dc(const PrefillArgs& a, hipStream_t s) {
+  const int mask = (a.window > 0 ? 1 : 0) | (a.block_mask ? 2 : 0);
+  switch (mask) {
+    case 1: return launch_t<D, 1, CACHE>(a, s);
+    case 2: return launch_t<D, 2, CACHE>(a, s);
+    case 3: return launch_t<D, 3, CACHE>(a, s);
+    default: return launch_t<D, 0, CACHE>(a, s);
+  }
+}
+
+template <int D>
+static hipError_t launch_d(const PrefillArgs& a, hipStream_t s) {
+  return a.cache_lens ? launch_dc<D, true>(a, s) : launch_dc<D, false>(a, s);
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int d, hipStream_t s) {
   if ((long)a.B * a.G * a.n_blk <= 0) return hipSuccess;
-  return d == 128 ? launch_t<128>(a, s) : launch_t<64>(a, s);
+  return d == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
 }
 
 int prefill_bf16_cols_per_block() { return COLS; }

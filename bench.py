@@ -19,6 +19,9 @@ timed region. Prints one JSON line:
 * --workload chunked: gqa_prefill_cached on 4 sequences, each a 2048-token chunk after a
   cached prefix of U{2048..14336} tokens (H=32, G=8, d=128); FLOPs count every visible
   (new query, key) pair, cached keys included.
+* --workload long_window / long_blocks: the T=32768, H=64, G=4 prefill with a 512-key
+  sliding window, or with a 64-key block layout (each query block keeps its previous block
+  and 10% of the earlier ones, seed 9); FLOPs count only the visible (query, key) pairs.
 * --workload decode_loop: a generation loop, 16 sequences from cache lengths U{256..2048};
   each step advances seq_lens on the device and decodes one token per sequence. value = GB/s
   of the step replayed as one HIP graph (gqa_decode_graph_*); the eager step (a torch add and
@@ -42,7 +45,9 @@ FP32_PEAK_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
 
 WORKLOADS = ("default", "tiny_f32", "prefill_4k", "varlen", "decode", "long_g4", "long_g1",
-             "chunked", "decode_loop", "copy_calibration")
+             "long_window", "long_blocks", "chunked", "decode_loop", "copy_calibration")
+WINDOW = 512          # sliding-window workload: keys per query
+BLOCK_DENSITY = 0.1   # block-sparse workload: share of earlier 64-key blocks kept
 COPY_BYTES = 1 << 30  # bytes read (and written) per step of the copy calibration
 
 
@@ -85,11 +90,34 @@ def prefill_case(name):
     import workloads as W
     return {"tiny_f32": W.tiny_f32, "prefill_4k": W.prefill_4k, "default": W.prefill_4k,
             "varlen": W.prefill_varlen, "long_g4": lambda: W.prefill_long(4),
-            "long_g1": lambda: W.prefill_long(1)}[name]()
+            "long_g1": lambda: W.prefill_long(1), "long_window": lambda: W.prefill_long(4),
+            "long_blocks": lambda: W.prefill_long(4)}[name]()
+
+
+def visible_pairs(lengths, window=0, block_mask=None):
+    """(query, key) pairs a causal prefill with these masks must compute, per head: the
+    algorithmic work of the mask variants (64-key blocks, the diagonal block always kept)."""
+    import numpy as np
+    total = 0
+    for T in (int(t) for t in lengths):
+        i = np.arange(T, dtype=np.int64)
+        if block_mask is None:
+            lo = np.maximum(0, i - window + 1) if window else np.zeros(T, np.int64)
+            total += int(np.sum(i - lo + 1))
+            continue
+        for qb in range(-(-T // 64)):
+            rows = np.arange(64 * qb, min(T, 64 * qb + 64))
+            lo = np.maximum(0, rows - window + 1) if window else np.zeros(len(rows), np.int64)
+            kb = np.flatnonzero(block_mask[qb, :qb + 1] | (np.arange(qb + 1) == qb))
+            for k in kb:  # keys [64 k, 64 k + 64) intersected with [lo, row]
+                a = np.maximum(lo, 64 * k)
+                b = np.minimum(rows, 64 * k + 63)
+                total += int(np.sum(np.maximum(0, b - a + 1)))
+    return total
 
 
 class Prefill:
-    def __init__(self, case):
+    def __init__(self, case, window=0, block_mask=None):
         import torch
         import attention_head_qk_amd as gqa
         sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -102,11 +130,18 @@ class Prefill:
                                                   self.dev["q"].dtype), dtype=torch.uint8,
                               device="cuda")
         self.out = torch.empty_like(self.dev["q"])
+        self.window = window
+        self.block_mask = block_mask
+        self.masks = {}
+        if window:
+            self.masks["window"] = window
+        if block_mask is not None:
+            self.masks["block_mask"] = torch.from_numpy(gqa.pack_block_mask(block_mask)).cuda()
 
     def __call__(self, prof=None):
         c, dv = self.case, self.dev
         kw = dict(causal=c.causal, q_norm_w=dv["q_norm_w"], k_norm_w=dv["k_norm_w"], eps=c.eps,
-                  theta=c.theta, workspace=self.ws, prof=prof)
+                  theta=c.theta, workspace=self.ws, prof=prof, **self.masks)
         if c.dense:
             B, T = c.B, c.T_max
             return self.gqa.prefill(dv["q"].view(B, T, c.H, c.d), dv["k"].view(B, T, c.G, c.d),
@@ -117,7 +152,10 @@ class Prefill:
 
     @property
     def work(self):
-        return self.case.flops
+        if not self.masks:
+            return self.case.flops
+        c = self.case
+        return 4.0 * c.d * c.H * visible_pairs(c.lengths, self.window, self.block_mask)
 
 
 class PrefillCached:
@@ -382,6 +420,11 @@ def main(argv=None):
     if args.workload == "chunked":
         pre = PrefillCached(W.prefill_chunked())
         log(f"bench: cached prefill inputs ready ({pre.case.name}, N={pre.case.N})")
+    elif args.workload == "long_window":
+        pre = Prefill(prefill_case(args.workload), window=WINDOW)
+    elif args.workload == "long_blocks":
+        case = prefill_case(args.workload)
+        pre = Prefill(case, block_mask=W.make_block_mask(9, -(-case.T_max // 64), BLOCK_DENSITY))
     elif args.workload != "decode":
         pre = Prefill(prefill_case(args.workload))
         log(f"bench: prefill inputs ready ({pre.case.name}, N={pre.case.N})")
@@ -435,13 +478,20 @@ def main(argv=None):
                             "unit": "TFLOP/s", "frac": round(tf_kern / peak, 4),
                             "traffic": measured_traffic(kname, c.name),
                             "kernel": kname,
-                            "kernel_ms": round(kern_ms, 5), "flops_per_launch": c.flops}
+                            "kernel_ms": round(kern_ms, 5), "flops_per_launch": pre.work}
         line["prefill"] = {"ms": round(call_ms, 5), "tflops": round(tf_call, 3),
                            "frac_of_peak": round(tf_call / peak, 4)}
         cfg["prefill"] = {"name": c.name, "B": c.B, "lengths_sum": c.N, "T_max": c.T_max, "H": c.H,
                           "G": c.G, "d": c.d, "causal": c.causal, "seed": c.seed}
         if isinstance(pre, PrefillCached):
             cfg["prefill"].update(cache_lens=c.cache_lens.tolist(), max_seq=c.max_seq)
+        if getattr(pre, "window", 0):
+            cfg["prefill"]["window"] = pre.window
+            cfg["prefill"]["name"] = c.name + f"_window{pre.window}"
+        if getattr(pre, "block_mask", None) is not None:
+            cfg["prefill"]["block_mask"] = {"block": 64, "kept": int(pre.block_mask.sum()),
+                                            "density": BLOCK_DENSITY, "local": 1, "seed": 9}
+            cfg["prefill"]["name"] = c.name + "_blocks64"
     if dec is not None:
         c = dec.case
         call_ms, kern_ms = res["decode"]
@@ -462,7 +512,8 @@ def main(argv=None):
                          "roofline": line.pop("roofline_decode")})
     names = [v["name"] for v in cfg.values()]
     line["config"] = {"workload": " + ".join(names), **cfg}
-    if not args.no_cpu_baseline and pre is not None and not isinstance(pre, PrefillCached):
+    if (not args.no_cpu_baseline and pre is not None and not isinstance(pre, PrefillCached)
+            and not pre.masks):
         log("bench: timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline(pre.case)
     elif not args.no_cpu_baseline:

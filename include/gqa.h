@@ -40,7 +40,8 @@
  *       GQA_EINVAL    null required pointer, negative size, H, G or d <= 0, H % G != 0,
  *                     a device pointer not 16-byte aligned, an int array not 4-byte aligned;
  *       GQA_ENOTSUP   d not in {64, 128}, an unknown dtype, a bf16 prefill whose
- *                     T * G * d * 2 exceeds 2^31 - 1 bytes (one sequence's K rows), or a
+ *                     T * G * d * 2 exceeds 2^31 - 1 bytes (one sequence's K rows) or
+ *                     whose T * H / G exceeds 2^31 - 1 (its (position, head) columns), a
  *                     decode whose max_seq * G * d * element size exceeds 2^31 - 1 bytes
  *                     or max_seq exceeds 4096 splits of
  *                     gqa_decode_split_keys(B, H, G, max_seq) keys;
@@ -99,10 +100,21 @@ typedef struct gqa_params {
                                 main kernel (prefill attention, or the decode split pass);
                                 for callers that time that kernel alone. NULL = none       */
   void *prof_stop;           /* optional hipEvent_t, recorded right after that kernel       */
+  int window;                /* bf16 prefill (and cached prefill), causal only: > 0 keeps
+                                only the `window` most recent keys of each query (key index
+                                > query index - window); 0 = no window                     */
+  const uint32_t *block_mask; /* bf16 prefill (and cached prefill): optional device bit rows
+                                over 64-key blocks.  Row qb (query indices 64 qb .. 64 qb +
+                                63) has block_mask_words words; bit j of word w set = query
+                                block qb sees key block 32 w + j.  The diagonal block is
+                                always seen.  Rows: ceil(T / 64) for gqa_prefill, ceil(max_seq
+                                / 64) for gqa_prefill_cached; one mask serves every sequence
+                                (indices inside the sequence).  NULL = no block mask        */
+  int block_mask_words;      /* words per block_mask row, >= ceil(ceil(T_keys / 64) / 32)   */
 } gqa_params;
 
 /* Fills p with defaults: bf16, no norm weights, eps 1e-6, theta 1e6, scale 1/sqrt(d),
- * dense, no workspace, default stream, no profiling events. */
+ * dense, no workspace, default stream, no profiling events, no window, no block mask. */
 void gqa_params_init(gqa_params *p);
 
 /* Prefill (prompt) attention with the QK prologue.
@@ -112,6 +124,12 @@ void gqa_params_init(gqa_params *p);
  *   Dense: N = B*T and sequence b is tokens [b*T, (b+1)*T).  Packed: p->cu_seqlens given,
  *     N = cu_seqlens[B], sequence b is [cu[b], cu[b+1]) and T must be >= every length.
  *   causal: 1 = causal mask inside each sequence, 0 = every key of the sequence visible.
+ *   Mask variants (bf16 only; zizhi168.cn Qwen3 technical-report summary, section 3.1:
+ *   local attention inside a 512-token window, block-sparse attention over 64-token blocks):
+ *     p->window > 0 (needs causal = 1) and / or p->block_mask narrow the visible keys
+ *     further; key tiles no query of a workgroup sees are skipped.  GQA_EINVAL for a
+ *     negative window, a window without the causal mask, a misaligned block_mask or
+ *     block_mask_words too small for T; GQA_ENOTSUP for either with fp32.
  *   Needs p->workspace of gqa_workspace_bytes(GQA_OP_PREFILL, B, T, H, G, d, dtype). */
 gqa_status gqa_prefill(const void *q, const void *k, const void *v, const int32_t *positions,
                        void *out, int B, int T, int H, int G, int d, int causal,
@@ -128,7 +146,9 @@ gqa_status gqa_prefill(const void *q, const void *k, const void *v, const int32_
  *   step (6)), then with causal = 1 it attends to keys 0 .. cache_lens[b] + t of its sequence
  *   (D1-5 with the query at key index cache_lens[b] + t); causal = 0: to all
  *   cache_lens[b] + T_b keys.  out [N, H, d].  cache_lens[b] + T_b <= max_seq is the
- *   caller's to ensure: rows past max_seq are neither written nor read.  No workspace;
+ *   caller's to ensure: rows past max_seq are neither written nor read.  p->window and
+ *   p->block_mask work as in gqa_prefill over key indices of the whole sequence (cache rows
+ *   first), the block mask with ceil(max_seq / 64) rows.  No workspace;
  *   p->k_out, k_new and v_new are not used.  GQA_ENOTSUP for fp32 and when
  *   max_seq * G * d * 2 exceeds 2^31 - 1 bytes. */
 gqa_status gqa_prefill_cached(const void *q, const void *k, const void *v, void *k_cache,
@@ -142,6 +162,7 @@ gqa_status gqa_prefill_cached(const void *q, const void *k, const void *v, void 
  *     K rows are post-prologue.  With p->k_new and p->v_new the new row is written at
  *     slot seq_lens[b]-1 first (so k_cache and v_cache are written only then).
  *   seq_lens: device [B], 0 <= seq_lens[b] <= max_seq, counting the new token.
+ *   p->window and p->block_mask are not supported here (GQA_ENOTSUP when set).
  *   Needs p->workspace of gqa_workspace_bytes(GQA_OP_DECODE, B, max_seq, H, G, d, dtype). */
 gqa_status gqa_decode(const void *q, void *k_cache, void *v_cache, const int32_t *seq_lens,
                       void *out, int B, int H, int G, int d, int max_seq,

@@ -99,9 +99,9 @@ def softmax_rows(S: np.ndarray) -> np.ndarray:
 
 
 def visible_keys(Tq: int, Tk: int, causal: bool, window: int = 0, block_mask=None,
-                 block: int = 64) -> np.ndarray:
+                 block: int = 64, q_index=None) -> np.ndarray:
     """Boolean [Tq, Tk]: which keys each query row may see. Query row r sits at key index
-    i = r + (Tk - Tq); key index j.
+    i = r + (Tk - Tq) (or i = q_index[r] when given); key index j.
 
     * causal: j <= i (Qwen3 series 1, D1-5).
     * window W > 0: also j > i - W, the W most recent keys including itself (zizhi168.cn
@@ -109,7 +109,10 @@ def visible_keys(Tq: int, Tk: int, causal: bool, window: int = 0, block_mask=Non
     * block_mask [n_blocks, n_blocks] of bools: also block_mask[i // block, j // block], with
       the diagonal block always kept so that every row sees itself (same section:
       block-sparse attention over 64-token blocks)."""
-    i = np.arange(Tq)[:, None] + (Tk - Tq)
+    if q_index is None:
+        i = np.arange(Tq)[:, None] + (Tk - Tq)
+    else:
+        i = np.asarray(q_index, dtype=np.int64)[:, None]
     j = np.arange(Tk)[None, :]
     vis = np.ones((Tq, Tk), dtype=bool)
     if causal:
@@ -201,7 +204,7 @@ def prefill_rows(q, k, v, positions, cu_seqlens, rows, q_norm_w, k_norm_w, eps, 
         qt = rope(rms_norm(np.asarray(q[t:t + 1], np.float64), q_norm_w, eps),
                   positions[t:t + 1], theta)[0]
         r = int(t - s)
-        vis = visible_keys(e - s, e - s, causal, window, block_mask, block)[r]
+        vis = visible_keys(1, e - s, causal, window, block_mask, block, q_index=[r])[0]
         vb = np.asarray(v[s:e], np.float64)[vis]
         for i in range(H):
             g = i // h

@@ -75,18 +75,25 @@ def run_prefill(case: W.PrefillCase, dev=None, packed=None, pass_positions=True,
     return out
 
 
-def oracle_prefill(case: W.PrefillCase):
+def oracle_prefill(case: W.PrefillCase, **masks):
+    """masks: window / block_mask (boolean layout) as the oracle takes them."""
     from oracle import gqa_oracle as O
     return O.prefill(case.f64("q"), case.f64("k"), case.f64("v"), case.positions,
                      case.cu_seqlens, case.f64("q_norm_w"), case.f64("k_norm_w"), case.eps,
-                     case.theta, case.causal)
+                     case.theta, case.causal, **masks)
 
 
-def oracle_prefill_rows(case: W.PrefillCase, rows):
+def oracle_prefill_rows(case: W.PrefillCase, rows, **masks):
     from oracle import gqa_oracle as O
     return O.prefill_rows(case.f64("q"), case.f64("k"), case.f64("v"), case.positions,
                           case.cu_seqlens, rows, case.f64("q_norm_w"), case.f64("k_norm_w"),
-                          case.eps, case.theta, case.causal)
+                          case.eps, case.theta, case.causal, **masks)
+
+
+def device_block_mask(mask: np.ndarray) -> torch.Tensor:
+    """Boolean layout -> the library's device bit rows (packed by the binding's helper)."""
+    import attention_head_qk_amd as gqa
+    return torch.from_numpy(np.ascontiguousarray(gqa.pack_block_mask(mask))).cuda()
 
 
 def sample_rows(case: W.PrefillCase, n_random: int, seed: int = 0, tile: int = 64):
@@ -183,7 +190,7 @@ def run_prefill_cached(case: W.CachedPrefillCase, dev, packed=None, pass_positio
                               dev["v"].view(B, T, G, d), *args, **common).view(-1, H, d)
 
 
-def oracle_prefill_cached_seq(case: W.CachedPrefillCase, b: int, positions=None):
+def oracle_prefill_cached_seq(case: W.CachedPrefillCase, b: int, positions=None, **masks):
     """Oracle of one sequence: (out [T_b, H, d], K rows [past + T_b, G, d], V rows)."""
     from oracle import gqa_oracle as O
     s, e = int(case.cu_seqlens[b]), int(case.cu_seqlens[b + 1])
@@ -197,7 +204,7 @@ def oracle_prefill_cached_seq(case: W.CachedPrefillCase, b: int, positions=None)
     out, kc2, vc2 = O.prefill_cached(case.f64("q")[s:e], case.f64("k")[s:e], case.f64("v")[s:e],
                                      kc, vc, [past], np.array([0, e - s]), case.f64("q_norm_w"),
                                      case.f64("k_norm_w"), case.eps, case.theta, positions=pos,
-                                     causal=case.causal)
+                                     causal=case.causal, **masks)
     return out, kc2[0], vc2[0]
 
 

@@ -38,6 +38,46 @@ def test_library_exports_every_declared_symbol():
     assert set(declared_functions()) == set(_lib.SIGNATURES)
 
 
+def test_params_layout_matches_header(tmp_path):
+    # the ctypes mirror of gqa_params must have the header's size and field offsets
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = [f[0] for f in _lib.GqaParams._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"gqa.h\"\nint main(void){\n"
+                   + 'printf("size %zu\\n", sizeof(gqa_params));\n'
+                   + "".join(f'printf("{f} %zu\\n", offsetof(gqa_params, {f}));\n' for f in fields)
+                   + "return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                      check=True).stdout.splitlines())
+    assert int(out["size"]) == ctypes.sizeof(_lib.GqaParams)
+    for f in fields:
+        assert int(out[f]) == getattr(_lib.GqaParams, f).offset, f
+
+
+def test_params_init_clears_masks():
+    p = _lib.default_params()
+    assert p.window == 0 and not p.block_mask and p.block_mask_words == 0
+
+
+def test_pack_block_mask_bits():
+    import numpy as np
+    from attention_head_qk_amd import pack_block_mask
+    rng = np.random.default_rng(5)
+    m = rng.random((7, 70)) < 0.3
+    w = pack_block_mask(m).view(np.uint32)
+    assert w.shape == (7, 3)
+    for qb in range(7):
+        for kb in range(96):
+            bit = (int(w[qb, kb // 32]) >> (kb % 32)) & 1
+            assert bit == (1 if kb < 70 and m[qb, kb] else 0)
+
+
 def test_status_strings():
     for code, tag in [(0, "GQA_OK"), (1, "GQA_EINVAL"), (2, "GQA_ENOTSUP"),
                       (3, "GQA_EWORKSPACE"), (4, "GQA_EHIP")]:
@@ -104,6 +144,25 @@ def _prefill(q=A, k=A, v=A, pos=None, out=A, B=1, T=8, H=4, G=2, d=128, causal=1
 def _decode(q=A, kc=A, vc=A, sl=A, out=A, B=2, H=4, G=2, d=128, S=16, **kw):
     p = _params(**kw)
     return _lib.load().gqa_decode(q, kc, vc, sl, out, B, H, G, d, S, ctypes.byref(p))
+
+
+def test_prefill_mask_checks():
+    # window needs the causal mask and a non-negative size; block_mask needs 4-byte alignment
+    # and rows wide enough for T keys; both are bf16 only
+    assert _prefill(window=-1) == _lib.GQA_EINVAL
+    assert _prefill(window=4, causal=0) == _lib.GQA_EINVAL
+    assert _prefill(block_mask=A + 2, block_mask_words=1) == _lib.GQA_EINVAL
+    assert _prefill(block_mask=A, block_mask_words=0) == _lib.GQA_EINVAL
+    assert _prefill(T=2049, block_mask=A, block_mask_words=1) == _lib.GQA_EINVAL  # 33 blocks
+    assert _prefill(T=2048, block_mask=A, block_mask_words=1, B=0) == _lib.GQA_OK
+    assert _prefill(window=4, dtype=_lib.GQA_F32) == _lib.GQA_ENOTSUP
+    assert _prefill(block_mask=A, block_mask_words=1, dtype=_lib.GQA_F32) == _lib.GQA_ENOTSUP
+    assert _prefill(window=4, B=0) == _lib.GQA_OK
+    assert _prefill_cached(window=4, causal=0) == _lib.GQA_EINVAL
+    assert _prefill_cached(S=2049, block_mask=A, block_mask_words=1) == _lib.GQA_EINVAL
+    assert _prefill_cached(window=3, B=0) == _lib.GQA_OK
+    assert _decode(window=8) == _lib.GQA_ENOTSUP
+    assert _decode(block_mask=A, block_mask_words=4) == _lib.GQA_ENOTSUP
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -1,0 +1,149 @@
+"""GPU parity of the mask variants of the bf16 prefill (sliding window, 64-key block layout,
+both) against the fp64 oracle, element by element on small ragged shapes and at 4096 tokens,
+on sampled rows at 32768 tokens; plus the invariants that tie them to the plain kernel
+(a window covering the sequence, or a full layout, changes no bit)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+
+from _gpu import (check, device_block_mask, device_cached_inputs, device_prefill_inputs,
+                  oracle_prefill, oracle_prefill_cached_seq, oracle_prefill_rows, run_prefill,
+                  run_prefill_cached, sample_rows, say, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+
+def _nb(T):
+    return max(1, -(-T // 64))
+
+
+WINDOW_SHAPES = [
+    # (lengths, H, G, d, window)
+    ([300], 16, 8, 128, 1),          # only the diagonal
+    ([300], 16, 8, 128, 37),
+    ([300], 16, 8, 128, 64),
+    ([300], 16, 8, 128, 100),
+    ([300], 8, 8, 128, 100),         # h = 1: a workgroup spans 128 positions
+    ([257], 64, 1, 128, 70),         # MQA
+    ([190], 16, 4, 64, 70),          # d = 64
+    ([1, 63, 64, 65, 0, 129, 200], 32, 8, 128, 50),  # packed, ragged, an empty sequence
+]
+
+
+@pytest.mark.parametrize("lengths,H,G,d,window", WINDOW_SHAPES)
+def test_window_full(lengths, H, G, d, window):
+    case = W.make_prefill(f"win_{lengths}_{H}_{G}_{d}_{window}", 120 + H + G + d + window,
+                          lengths=lengths, H=H, G=G, d=d)
+    say("prefill window", case.name)
+    got = to_f64(run_prefill(case, window=window))
+    check(got, oracle_prefill(case, window=window), W.BF16, case.name)
+
+
+BLOCK_SHAPES = [
+    # (lengths, H, G, d, density, causal)
+    ([333], 16, 8, 128, 0.3, True),   # h = 2: one query block per workgroup
+    ([257], 8, 8, 128, 0.3, True),    # h = 1: two query blocks per workgroup
+    ([150], 64, 1, 128, 0.5, True),   # MQA
+    ([100, 1, 200, 64], 16, 4, 128, 0.4, True),
+    ([260], 8, 8, 128, 0.0, True),    # diagonal blocks only
+    ([190], 16, 4, 64, 0.3, True),    # d = 64
+    ([130], 32, 8, 128, 0.4, False),  # no causal mask: later blocks too
+]
+
+
+@pytest.mark.parametrize("lengths,H,G,d,density,causal", BLOCK_SHAPES)
+def test_block_mask_full(lengths, H, G, d, density, causal):
+    case = W.make_prefill(f"blk_{lengths}_{H}_{G}_{d}_{density}", 140 + H + G + d,
+                          lengths=lengths, H=H, G=G, d=d, causal=causal)
+    nb = _nb(max(lengths))
+    bm = W.make_block_mask(141 + H, nb, density, causal=causal)
+    say("prefill block mask", case.name, "kept", int(bm.sum()), "of", nb * nb)
+    got = to_f64(run_prefill(case, block_mask=device_block_mask(bm)))
+    check(got, oracle_prefill(case, block_mask=bm), W.BF16, case.name)
+
+
+@pytest.mark.parametrize("lengths,H,G", [([400], 16, 4), ([300], 8, 8)])
+def test_window_and_block_mask_full(lengths, H, G):
+    case = W.make_prefill(f"winblk_{lengths}_{H}_{G}", 160 + H + G, lengths=lengths, H=H, G=G)
+    bm = W.make_block_mask(161, _nb(max(lengths)), 0.4)
+    say("prefill window + block mask", case.name)
+    got = to_f64(run_prefill(case, window=150, block_mask=device_block_mask(bm)))
+    check(got, oracle_prefill(case, window=150, block_mask=bm), W.BF16, case.name)
+
+
+def test_window_4k_full():
+    case = W.prefill_4k()
+    say("prefill window 512 at T=4096")
+    got = to_f64(run_prefill(case, window=512))
+    check(got, oracle_prefill(case, window=512), W.BF16, case.name)
+
+
+@pytest.mark.parametrize("kind", ["window", "blocks"])
+def test_long_32k_sampled_rows(kind):
+    case = W.prefill_long(4)
+    rows = sample_rows(case, 24, seed=7)
+    if kind == "window":
+        masks = dict(window=512)
+        dev_masks = dict(window=512)
+    else:
+        bm = W.make_block_mask(171, _nb(case.T_max), 0.1)
+        masks = dict(block_mask=bm)
+        dev_masks = dict(block_mask=device_block_mask(bm))
+    say("prefill long T=32768 H=64 G=4", kind)
+    got = to_f64(run_prefill(case, **dev_masks))
+    check(got[rows], oracle_prefill_rows(case, rows, **masks), W.BF16, case.name + " " + kind)
+
+
+def test_cached_prefill_with_masks():
+    case = W.make_cached_prefill("cached_masks", 180, [100, 37], [150, 64], 320, H=16, G=8)
+    bm = W.make_block_mask(181, _nb(case.max_seq), 0.4)
+    dev = device_cached_inputs(case)
+    say("prefill cached with window + block mask")
+    got = to_f64(run_prefill_cached(case, dev, window=90, block_mask=device_block_mask(bm)))
+    for b in range(case.B):
+        s, e = int(case.cu_seqlens[b]), int(case.cu_seqlens[b + 1])
+        want, _, _ = oracle_prefill_cached_seq(case, b, window=90, block_mask=bm)
+        check(got[s:e], want, W.BF16, f"b={b}")
+
+
+def test_wide_masks_change_no_bit():
+    # a window of at least the sequence, or a layout with every block kept, visits the same
+    # tiles in the same order as the plain kernel: the outputs are bit-identical
+    case = W.make_prefill("wide", 190, lengths=[700], H=16, G=8)
+    dev = device_prefill_inputs(case)
+    say("prefill wide masks vs plain")
+    plain = run_prefill(case, dev=dev)
+    full = np.ones((_nb(700), _nb(700)), dtype=bool)
+    assert torch.equal(run_prefill(case, dev=dev, window=700), plain)
+    assert torch.equal(run_prefill(case, dev=dev, window=100000), plain)
+    assert torch.equal(run_prefill(case, dev=dev, block_mask=device_block_mask(full)), plain)
+
+
+@pytest.mark.parametrize("sign", ["neg", "mixed"])
+def test_window_extreme_scores(sign):
+    # equal scores of +-200 in log2 units (see the plain kernel's extreme test): the exact
+    # path must engage also when some columns of a wave have seen no key yet
+    case = W.make_prefill("win_extreme_" + sign, 191, lengths=[300], H=8, G=8,
+                          positions=np.zeros(300, np.int32))
+    rng = np.random.default_rng(192)
+    x = rng.standard_normal(case.d).astype(np.float32)
+    sgn = {"neg": -np.ones(case.H), "mixed": np.where(np.arange(case.H) % 2 == 0, 1.0, -1.0)}[sign]
+    q = np.broadcast_to(x[None, None, :] * sgn.astype(np.float32)[None, :, None],
+                        (case.N, case.H, case.d))
+    k = np.broadcast_to(x[None, None, :], (case.N, case.G, case.d))
+    case.q = W.encode(np.ascontiguousarray(q), W.BF16)
+    case.k = W.encode(np.ascontiguousarray(k), W.BF16)
+    g = np.full(case.d, 3.5, np.float32)
+    case.q_norm_w = W.encode(g, W.BF16)
+    case.k_norm_w = W.encode(g, W.BF16)
+    say("prefill window extreme scores", sign)
+    got = to_f64(run_prefill(case, window=100))
+    want = oracle_prefill(case, window=100)
+    v = case.f64("v")
+    # equal scores: each row is the mean of V over its window (the closed form)
+    for t in (0, 50, 99, 100, 299):
+        lo = max(0, t - 99)
+        assert np.allclose(want[t], np.repeat(v[lo:t + 1].mean(axis=0), 1, axis=0), atol=1e-9)
+    check(got, want, W.BF16, "window extreme " + sign)

@@ -242,6 +242,23 @@ def make_decode(name, seed, B=64, len_range=(1024, 32768), max_seq=32768, H=32, 
                       q_norm_w=gq, k_norm_w=gk)
 
 
+# ----------------------------------------------------------------------------- block layouts
+def make_block_mask(seed, n_blocks, density, local=1, causal=True) -> np.ndarray:
+    """Seeded boolean key-block layout [n_blocks, n_blocks] for the block-sparse mask: query
+    block qb keeps its ``local`` preceding key blocks and each other earlier block (any
+    block, without ``causal``) with probability ``density``; the diagonal is left to the
+    mask's own rule. Drawn from ``default_rng(seed)``: one uniform per entry, row-major."""
+    rng = np.random.default_rng(seed)
+    u = rng.random((n_blocks, n_blocks))
+    qb = np.arange(n_blocks)[:, None]
+    kb = np.arange(n_blocks)[None, :]
+    keep = u < density
+    if causal:
+        keep &= kb < qb
+    keep |= (kb < qb) & (kb >= qb - local)
+    return keep
+
+
 # ----------------------------------------------------------------------------- decode loop
 @dataclasses.dataclass
 class DecodeStepsCase:
