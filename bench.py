@@ -472,26 +472,29 @@ def main(argv=None):
         tf_kern = pre.work / (kern_ms * 1e-3) / 1e12
         peak = FP32_PEAK_TFLOPS if c.dtype == W.F32 else MFMA_BF16_PEAK_TFLOPS
         kname = "prefill_bf16_kernel" if c.dtype == W.BF16 else "prefill_f32_kernel"
+        wname = c.name
+        if getattr(pre, "window", 0):
+            wname += f"_window{pre.window}"
+        if getattr(pre, "block_mask", None) is not None:
+            wname += "_blocks64"
         line.update({"value": round(tf_call, 3), "unit": "TFLOP/s",
                      "dtype": "f32" if c.dtype == W.F32 else "bf16"})
         line["roofline"] = {"bound": "mfma", "achieved": round(tf_kern, 3), "peak": peak,
                             "unit": "TFLOP/s", "frac": round(tf_kern / peak, 4),
-                            "traffic": measured_traffic(kname, c.name),
+                            "traffic": measured_traffic(kname, wname),
                             "kernel": kname,
                             "kernel_ms": round(kern_ms, 5), "flops_per_launch": pre.work}
         line["prefill"] = {"ms": round(call_ms, 5), "tflops": round(tf_call, 3),
                            "frac_of_peak": round(tf_call / peak, 4)}
-        cfg["prefill"] = {"name": c.name, "B": c.B, "lengths_sum": c.N, "T_max": c.T_max, "H": c.H,
+        cfg["prefill"] = {"name": wname, "B": c.B, "lengths_sum": c.N, "T_max": c.T_max, "H": c.H,
                           "G": c.G, "d": c.d, "causal": c.causal, "seed": c.seed}
         if isinstance(pre, PrefillCached):
             cfg["prefill"].update(cache_lens=c.cache_lens.tolist(), max_seq=c.max_seq)
         if getattr(pre, "window", 0):
             cfg["prefill"]["window"] = pre.window
-            cfg["prefill"]["name"] = c.name + f"_window{pre.window}"
         if getattr(pre, "block_mask", None) is not None:
             cfg["prefill"]["block_mask"] = {"block": 64, "kept": int(pre.block_mask.sum()),
                                             "density": BLOCK_DENSITY, "local": 1, "seed": 9}
-            cfg["prefill"]["name"] = c.name + "_blocks64"
     if dec is not None:
         c = dec.case
         call_ms, kern_ms = res["decode"]
