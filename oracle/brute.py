@@ -25,10 +25,12 @@ def rmsnorm_vec(x, gamma, eps):
 
 
 def rope_matrix(pos, d, theta):
-    """The d x d block-diagonal rotation matrix R(pos)."""
+    """The d x d block-diagonal rotation matrix R(pos). ``theta`` is the base, or a list of
+    the d/2 block frequencies."""
     R = [[0.0] * d for _ in range(d)]
     for j in range(d // 2):
-        a = pos * theta ** (-2.0 * j / d)
+        w = theta[j] if isinstance(theta, (list, tuple)) else theta ** (-2.0 * j / d)
+        a = pos * w
         c, s = math.cos(a), math.sin(a)
         R[2 * j][2 * j] = c
         R[2 * j][2 * j + 1] = -s
@@ -43,7 +45,7 @@ def matvec(M, x):
 
 def prologue_vec(x, pos, gamma, eps, theta):
     y = rmsnorm_vec(x, gamma, eps)
-    if theta == 0:
+    if not isinstance(theta, (list, tuple)) and theta == 0:
         return y
     return matvec(rope_matrix(pos, len(x), theta), y)
 

@@ -52,18 +52,30 @@ def rope_inv_freq(d: int, theta: float) -> np.ndarray:
     return np.power(float(theta), -2.0 * j / d)
 
 
-def rope(x: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray:
+def inv_freq_of(d: int, theta) -> np.ndarray:
+    """The d/2 RoPE frequencies: ``theta`` is the base (``rope_inv_freq``) or already a table
+    of d/2 frequencies (a scaled variant below)."""
+    if np.ndim(theta) == 0:
+        return rope_inv_freq(d, float(theta))
+    w = np.asarray(theta, dtype=np.float64)
+    if w.shape != (d // 2,):
+        raise ValueError("a frequency table needs d/2 entries")
+    return w
+
+
+def rope(x: np.ndarray, positions: np.ndarray, theta) -> np.ndarray:
     """Rotate each adjacent pair (x_2j, x_2j+1) of x[t, head, :] counter-clockwise by
     positions[t] * omega_j.
 
     Qwen3 series 1, D2-2 (R(pos) is block-diagonal with 2x2 rotation blocks
     [[cos, -sin], [sin, cos]] of angle pos*theta_j); Qwen3 architecture, 3.1.2 (pairs are
-    the even/odd elements, rotated as a complex product). ``theta == 0`` skips RoPE."""
+    the even/odd elements, rotated as a complex product). ``theta`` is the base (0 skips
+    RoPE) or a table of the d/2 frequencies. Positions may be fractional."""
     x = np.asarray(x, dtype=np.float64)
-    if theta == 0:
+    if np.ndim(theta) == 0 and theta == 0:
         return x.copy()
     d = x.shape[-1]
-    phi = np.asarray(positions, dtype=np.float64)[:, None] * rope_inv_freq(d, theta)[None, :]
+    phi = np.asarray(positions, dtype=np.float64)[:, None] * inv_freq_of(d, theta)[None, :]
     c = np.cos(phi)[:, None, :]
     s = np.sin(phi)[:, None, :]
     a = x[..., 0::2]
@@ -72,6 +84,31 @@ def rope(x: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray:
     y[..., 0::2] = a * c - b * s
     y[..., 1::2] = a * s + b * c
     return y
+
+
+# Scaled frequency tables (each passed as ``theta`` wherever a base is taken).
+def inv_freq_linear(d: int, theta: float, alpha: float) -> np.ndarray:
+    """Linear position interpolation: every position index divided by the extension factor
+    alpha (zizhi168.cn technical-report summary, §4.2), i.e. every frequency divided by it."""
+    return rope_inv_freq(d, theta) / float(alpha)
+
+
+def inv_freq_yarn_page(d: int, theta: float, train_len: int, infer_len: int,
+                       scale: float = 1.0) -> np.ndarray:
+    """The frequency scaling that Qwen3 architecture, 3.4.2 prints under the name YaRN: past
+    the training length, s = scale * log2(infer_len / train_len) and omega_j is multiplied by
+    1 - s * 2j / d; otherwise the frequencies are unchanged."""
+    w = rope_inv_freq(d, theta)
+    if infer_len > train_len:
+        s = float(scale) * np.log(infer_len / train_len) / np.log(2.0)
+        w = w * (1.0 - s * (2.0 * np.arange(d // 2, dtype=np.float64) / d))
+    return w
+
+
+def ntk_theta(theta: float, alpha: float, d: int) -> float:
+    """NTK-aware scaling (summary, §4.2) read as a change of base: theta' = theta *
+    alpha^(d / (d - 2)), which keeps the highest frequency and divides the lowest by alpha."""
+    return float(theta) * float(alpha) ** (d / (d - 2.0))
 
 
 def qk_norm_rope(q, k, positions, q_norm_w, k_norm_w, eps, theta):

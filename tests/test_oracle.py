@@ -626,3 +626,61 @@ def test_masks_in_cached_prefill_count_cache_rows():
                                  np.array([0, T - past]), gq, gk, 1e-6, 1e6, window=W,
                                  block_mask=bm, block=blk)
     assert np.allclose(out, full[past:], atol=1e-12, rtol=0)
+
+
+# ----------------------------------------------------------------------------- RoPE frequency variants
+def test_frequency_table_of_the_base_is_the_base_path():
+    rng = np.random.default_rng(400)
+    q, k, v, cu, pos, gq, gk = _case(rng, [9], H=4, G=2, d=8)
+    a = O.prefill(q, k, v, pos, cu, gq, gk, 1e-6, 1e6)
+    b = O.prefill(q, k, v, pos, cu, gq, gk, 1e-6, O.rope_inv_freq(8, 1e6))
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("alpha", [2.0, 4.0, 3.5])
+def test_linear_interpolation_divides_positions(alpha):
+    # summary §4.2: the position index divided by alpha; as a table, every frequency / alpha
+    rng = np.random.default_rng(410)
+    q, k, v, cu, pos, gq, gk = _case(rng, [11], H=4, G=2, d=8)
+    pos = np.arange(11) * 3 + 5
+    a = O.prefill(q, k, v, pos, cu, gq, gk, 1e-6, O.inv_freq_linear(8, 1e4, alpha))
+    b = O.prefill(q, k, v, pos / alpha, cu, gq, gk, 1e-6, 1e4)
+    assert np.allclose(a, b, atol=1e-12, rtol=0)
+
+
+def test_yarn_page_formula_hand_values():
+    # d = 8, theta = 1e4: omega = (1, 0.1, 0.01, 0.001); train 2048 -> infer 8192, scale 1:
+    # s = log2(4) = 2, factors 1 - 2 * (0, 2, 4, 6) / 8 = (1, 0.5, 0, -0.5)
+    w = O.inv_freq_yarn_page(8, 1e4, 2048, 8192)
+    assert np.allclose(w, [1.0, 0.05, 0.0, -0.0005], atol=1e-15, rtol=1e-12)
+    w = O.inv_freq_yarn_page(8, 1e4, 2048, 4096, scale=0.5)  # s = 0.5
+    assert np.allclose(w, [1.0, 0.1 * 0.875, 0.01 * 0.75, 0.001 * 0.625], rtol=1e-12)
+    assert np.array_equal(O.inv_freq_yarn_page(8, 1e4, 4096, 4096), O.rope_inv_freq(8, 1e4))
+
+
+def test_ntk_base_change_keeps_highest_divides_lowest():
+    for d, alpha in ((8, 4.0), (128, 2.0), (64, 8.0)):
+        w0 = O.rope_inv_freq(d, 1e6)
+        w1 = O.rope_inv_freq(d, O.ntk_theta(1e6, alpha, d))
+        assert w1[0] == w0[0] == 1.0
+        assert np.isclose(w1[-1], w0[-1] / alpha, rtol=1e-12)
+
+
+def test_frequency_tables_match_brute_force():
+    # a scaled table through prefill and decode against the brute force with explicit R(pos)
+    rng = np.random.default_rng(420)
+    T, H, G, d = 7, 4, 2, 8
+    q, k, v, cu, pos, gq, gk = _case(rng, [T], H=H, G=G, d=d)
+    pos = np.array([0, 3, 4, 9, 10, 100, 1000])
+    for w in (O.inv_freq_yarn_page(d, 1e4, 2048, 8192), O.inv_freq_linear(d, 1e4, 4.0)):
+        out = O.prefill(q, k, v, pos, cu, gq, gk, 1e-6, w)
+        want = brute.gqa_prefill(q.tolist(), k.tolist(), v.tolist(), pos.tolist(), gq.tolist(),
+                                 gk.tolist(), 1e-6, w.tolist())
+        assert np.allclose(out, np.array(want), atol=1e-12, rtol=0)
+        kc, vc = _cache_from_prefix(q, k, v, pos, gq, gk, 0, T)  # empty cache
+        _, kt = O.qk_norm_rope(q[:T - 1], k[:T - 1], pos[:T - 1], gq, gk, 1e-6, w)
+        kc[0, :T - 1] = kt
+        vc[0, :T - 1] = v[:T - 1]
+        dec, _, _ = O.decode_one(q[T - 1], kc[0], vc[0], T, gq, gk, 1e-6, w, position=pos[T - 1],
+                                 k_new=k[T - 1], v_new=v[T - 1])
+        assert np.allclose(dec, out[T - 1], atol=1e-12, rtol=0)
