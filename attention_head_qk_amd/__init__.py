@@ -23,7 +23,7 @@ from ._lib import GqaError  # noqa: F401
 _lib.load()  # fail at import, loudly, if the HIP library is not built
 
 __all__ = ["prefill", "prefill_cached", "decode", "DecodeGraph", "qk_norm_rope", "workspace_bytes",
-           "decode_split_keys", "pack_block_mask", "GqaError"]
+           "decode_split_keys", "pack_block_mask", "rope_freq_table", "GqaError"]
 
 _DTYPES = {torch.float32: _lib.GQA_F32, torch.bfloat16: _lib.GQA_BF16}
 
@@ -44,8 +44,13 @@ def _dev(t, name, dtype=None):
     return t
 
 
-def _params(dtype, q_norm_w, k_norm_w, eps, theta, scale, stream, device):
+def _params(dtype, q_norm_w, k_norm_w, eps, theta, scale, stream, device, rope_inv_freq=None):
     p = _lib.default_params()
+    if rope_inv_freq is not None:
+        import numpy as np
+        w = np.ascontiguousarray(np.asarray(rope_inv_freq, dtype=np.float64).ravel())
+        p._freqs = w  # kept alive with the struct: the library reads it during the call
+        p.rope_inv_freq = w.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
     p.dtype = _DTYPES[dtype]
     p.q_norm_w = _ptr(_dev(q_norm_w, "q_norm_w", dtype))
     p.k_norm_w = _ptr(_dev(k_norm_w, "k_norm_w", dtype))
@@ -89,6 +94,29 @@ def _workspace(ws, nbytes, device):
     return ws
 
 
+def rope_freq_table(d, theta=1e6, kind="base", alpha=1.0, train_len=None, infer_len=None,
+                    scale=1.0):
+    """The d/2 RoPE frequencies for ``rope_inv_freq`` (host, float64):
+    base   omega_j = theta^(-2j/d);
+    linear position interpolation by the extension factor alpha: omega_j / alpha;
+    yarn   the architecture article's 3.4.2 formula: past train_len, omega_j times
+           1 - s 2j/d with s = scale * log2(infer_len / train_len);
+    ntk    NTK-aware scaling as a change of base, theta * alpha^(d / (d - 2))."""
+    import numpy as np
+    j = np.arange(d // 2, dtype=np.float64)
+    if kind == "ntk":
+        theta = float(theta) * float(alpha) ** (d / (d - 2.0))
+    w = float(theta) ** (-2.0 * j / d)
+    if kind == "linear":
+        w = w / float(alpha)
+    elif kind == "yarn":
+        if infer_len > train_len:
+            w = w * (1.0 - float(scale) * np.log2(infer_len / train_len) * 2.0 * j / d)
+    elif kind not in ("base", "ntk"):
+        raise ValueError(f"unknown RoPE scaling {kind!r}")
+    return w
+
+
 def pack_block_mask(mask):
     """Bit rows of gqa_params.block_mask from a boolean [query blocks, key blocks] array
     (host, numpy): word w of row qb holds key blocks 32 w .. 32 w + 31, bit j = block
@@ -116,14 +144,16 @@ def _masks(p, window, block_mask):
 
 def prefill(q, k, v, positions=None, *, causal=True, q_norm_w=None, k_norm_w=None, eps=1e-6,
             theta=1e6, scale=0.0, cu_seqlens=None, max_seqlen=None, k_out=None, out=None,
-            workspace=None, stream=None, prof=None, window=0, block_mask=None):
+            workspace=None, stream=None, prof=None, window=0, block_mask=None,
+            rope_inv_freq=None):
     """gqa_prefill. Dense: q [B, T, H, d], k/v [B, T, G, d]. Packed: q [N, H, d], k/v
     [N, G, d] with cu_seqlens (device int32 [B+1]) and max_seqlen >= every length.
     positions: optional device int32 [N] (RoPE positions; default 0..T_b-1 per sequence).
     k_out: optional [N, G, d] receiving the normalised, rotated K. prof: optional
     (start, stop) torch.cuda.Event pair recorded around the attention kernel alone.
     window: keep only the `window` most recent keys (causal only); block_mask: device int32
-    bit rows over 64-key blocks (``pack_block_mask``). Returns out like q."""
+    bit rows over 64-key blocks (``pack_block_mask``). rope_inv_freq: optional d/2 RoPE
+    frequencies (``rope_freq_table``) in place of theta. Returns out like q."""
     _dev(q, "q")
     dtype = q.dtype
     _dev(k, "k", dtype)
@@ -150,7 +180,7 @@ def prefill(q, k, v, positions=None, *, causal=True, q_norm_w=None, k_norm_w=Non
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out", dtype)
-    p = _params(dtype, q_norm_w, k_norm_w, eps, theta, scale, stream, q.device)
+    p = _params(dtype, q_norm_w, k_norm_w, eps, theta, scale, stream, q.device, rope_inv_freq)
     nbytes = workspace_bytes("prefill", B, T, H, G, d, dtype)
     ws = _workspace(workspace, nbytes, q.device)
     p.workspace = _ptr(ws)
@@ -168,7 +198,7 @@ def prefill(q, k, v, positions=None, *, causal=True, q_norm_w=None, k_norm_w=Non
 def prefill_cached(q, k, v, k_cache, v_cache, cache_lens, positions=None, *, causal=True,
                    q_norm_w=None, k_norm_w=None, eps=1e-6, theta=1e6, scale=0.0,
                    cu_seqlens=None, max_seqlen=None, out=None, stream=None, prof=None,
-                   window=0, block_mask=None):
+                   window=0, block_mask=None, rope_inv_freq=None):
     """gqa_prefill_cached (bf16). New tokens of sequences that already have cache_lens[b]
     (device int32 [B]) tokens in k_cache / v_cache [B, max_seq, G, d]: dense q [B, T, H, d],
     k/v [B, T, G, d], or packed q [N, H, d], k/v [N, G, d] with cu_seqlens and max_seqlen.
@@ -207,7 +237,7 @@ def prefill_cached(q, k, v, k_cache, v_cache, cache_lens, positions=None, *, cau
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out", dtype)
-    p = _params(dtype, q_norm_w, k_norm_w, eps, theta, scale, stream, q.device)
+    p = _params(dtype, q_norm_w, k_norm_w, eps, theta, scale, stream, q.device, rope_inv_freq)
     p.cu_seqlens = _ptr(cu_seqlens)
     _masks(p, window, block_mask)
     _prof(p, prof)
@@ -220,7 +250,7 @@ def prefill_cached(q, k, v, k_cache, v_cache, cache_lens, positions=None, *, cau
 
 def decode(q, k_cache, v_cache, seq_lens, *, k_new=None, v_new=None, positions=None,
            q_norm_w=None, k_norm_w=None, eps=1e-6, theta=1e6, scale=0.0, out=None,
-           workspace=None, stream=None, prof=None):
+           workspace=None, stream=None, prof=None, rope_inv_freq=None):
     """gqa_decode. q [B, H, d]; caches [B, max_seq, G, d] (K post-prologue, V raw);
     seq_lens device int32 [B] counting the new token; optional k_new/v_new [B, G, d] are
     normalised/rotated (K) and written at slot seq_lens[b]-1 first. prof: optional
@@ -241,7 +271,7 @@ def decode(q, k_cache, v_cache, seq_lens, *, k_new=None, v_new=None, positions=N
     if out is None:
         out = torch.empty_like(q)
     _dev(out, "out", dtype)
-    p = _params(dtype, q_norm_w, k_norm_w, eps, theta, scale, stream, q.device)
+    p = _params(dtype, q_norm_w, k_norm_w, eps, theta, scale, stream, q.device, rope_inv_freq)
     nbytes = workspace_bytes("decode", B, S, H, G, d, dtype)
     ws = _workspace(workspace, nbytes, q.device)
     p.workspace = _ptr(ws)
@@ -269,7 +299,7 @@ class DecodeGraph:
 
     def __init__(self, q, k_cache, v_cache, seq_lens, k_new, v_new, *, positions=None,
                  q_norm_w=None, k_norm_w=None, eps=1e-6, theta=1e6, scale=0.0, out=None,
-                 workspace=None):
+                 workspace=None, rope_inv_freq=None):
         self._h = None
         _dev(q, "q")
         dtype = q.dtype
@@ -287,7 +317,7 @@ class DecodeGraph:
         if k_new.shape != (B, G, d) or v_new.shape != k_new.shape or seq_lens.numel() != B:
             raise ValueError("k_new / v_new must be [B, G, d] and seq_lens [B]")
         out = torch.empty_like(q) if out is None else _dev(out, "out", dtype)
-        p = _params(dtype, q_norm_w, k_norm_w, eps, theta, scale, None, q.device)
+        p = _params(dtype, q_norm_w, k_norm_w, eps, theta, scale, None, q.device, rope_inv_freq)
         ws = _workspace(workspace, workspace_bytes("decode", B, S, H, G, d, dtype), q.device)
         p.workspace = _ptr(ws)
         p.workspace_bytes = ws.numel() * ws.element_size()
@@ -335,7 +365,7 @@ class DecodeGraph:
 
 
 def qk_norm_rope(q, k=None, positions=None, *, q_norm_w=None, k_norm_w=None, eps=1e-6,
-                 theta=1e6, q_out=None, k_out=None, stream=None):
+                 theta=1e6, q_out=None, k_out=None, stream=None, rope_inv_freq=None):
     """gqa_qk_norm_rope: q [N, H, d] (and k [N, G, d]) -> normalised, rotated copies.
     positions: device int32 [N] or None for 0..N-1."""
     _dev(q, "q")
@@ -347,7 +377,7 @@ def qk_norm_rope(q, k=None, positions=None, *, q_norm_w=None, k_norm_w=None, eps
     q_out = torch.empty_like(q) if q_out is None else _dev(q_out, "q_out", dtype)
     if k is not None:
         k_out = torch.empty_like(k) if k_out is None else _dev(k_out, "k_out", dtype)
-    p = _params(dtype, q_norm_w, k_norm_w, eps, theta, 0.0, stream, q.device)
+    p = _params(dtype, q_norm_w, k_norm_w, eps, theta, 0.0, stream, q.device, rope_inv_freq)
     rc = _lib.load().gqa_qk_norm_rope(_ptr(q), _ptr(k), _ptr(positions), _ptr(q_out),
                                       _ptr(k_out), N, H, G, d, ctypes.byref(p))
     _lib.check(rc, "gqa_qk_norm_rope")

@@ -40,6 +40,7 @@ class GqaParams(ctypes.Structure):
         ("window", ctypes.c_int),
         ("block_mask", _vp),
         ("block_mask_words", ctypes.c_int),
+        ("rope_inv_freq", ctypes.POINTER(ctypes.c_double)),
     ]
 
 

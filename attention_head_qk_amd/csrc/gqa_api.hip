@@ -68,11 +68,25 @@ float eff_scale(const gqa_params* p, int d) {
   return p->scale > 0.f ? p->scale : (float)(1.0 / std::sqrt((double)d));
 }
 
+// RoPE frequencies into the kernel arguments: the caller's table when given, else
+// theta^(-2j/d) computed here in fp64.
 template <typename Args>
 void fill_rope(Args& a, const gqa_params* p, int d) {
-  a.use_rope = p->rope_theta > 0.0 ? 1 : 0;
-  for (int j = 0; j < gqa::kMaxHalfD; ++j)
-    a.omega[j] = (a.use_rope && j < d / 2) ? std::pow(p->rope_theta, -2.0 * j / d) : 0.0;
+  a.use_rope = (p->rope_inv_freq || p->rope_theta > 0.0) ? 1 : 0;
+  for (int j = 0; j < gqa::kMaxHalfD; ++j) {
+    double w = 0.0;
+    if (a.use_rope && j < d / 2)
+      w = p->rope_inv_freq ? p->rope_inv_freq[j] : std::pow(p->rope_theta, -2.0 * j / d);
+    a.omega[j] = w;
+  }
+}
+
+// A caller's frequency table must hold d/2 finite values.
+gqa_status check_rope_table(const gqa_params* p, int d) {
+  if (!p->rope_inv_freq) return GQA_OK;
+  for (int j = 0; j < d / 2; ++j)
+    if (!std::isfinite(p->rope_inv_freq[j])) return GQA_EINVAL;
+  return GQA_OK;
 }
 
 gqa_status from_hip(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_EHIP; }
@@ -107,6 +121,7 @@ gqa_status decode_check(const void* q, void* k_cache, void* v_cache, const int32
   gqa_status st = check_params(p);
   if (st != GQA_OK) return st;
   if ((st = check_heads(H, G, d)) != GQA_OK) return st;
+  if ((st = check_rope_table(p, d)) != GQA_OK) return st;
   if (B < 0 || max_seq < 0) return GQA_EINVAL;
   if (p->window != 0 || p->block_mask) return GQA_ENOTSUP;
   if (B == 0) return GQA_OK;
@@ -211,6 +226,7 @@ void gqa_params_init(gqa_params* p) {
   p->window = 0;
   p->block_mask = nullptr;
   p->block_mask_words = 0;
+  p->rope_inv_freq = nullptr;
 }
 
 const char* gqa_status_str(gqa_status s) {
@@ -252,6 +268,7 @@ gqa_status gqa_prefill(const void* q, const void* k, const void* v, const int32_
   gqa_status st = check_params(p);
   if (st != GQA_OK) return st;
   if ((st = check_heads(H, G, d)) != GQA_OK) return st;
+  if ((st = check_rope_table(p, d)) != GQA_OK) return st;
   if (B < 0 || T < 0 || (causal != 0 && causal != 1)) return GQA_EINVAL;
   if ((long long)B * T > 0x7fffffffLL) return GQA_EINVAL;
   // the bf16 kernel addresses one sequence's K/V rows of a group with 32-bit buffer offsets
@@ -341,6 +358,7 @@ gqa_status gqa_prefill_cached(const void* q, const void* k, const void* v, void*
   gqa_status st = check_params(p);
   if (st != GQA_OK) return st;
   if ((st = check_heads(H, G, d)) != GQA_OK) return st;
+  if ((st = check_rope_table(p, d)) != GQA_OK) return st;
   if (B < 0 || T < 0 || max_seq < 1 || (causal != 0 && causal != 1)) return GQA_EINVAL;
   if ((long long)B * T > 0x7fffffffLL) return GQA_EINVAL;
   if (p->dtype != GQA_BF16) return GQA_ENOTSUP;
@@ -481,6 +499,7 @@ gqa_status gqa_qk_norm_rope(const void* q, const void* k, const int32_t* positio
   gqa_status st = check_params(p);
   if (st != GQA_OK) return st;
   if ((st = check_heads(H, G, d)) != GQA_OK) return st;
+  if ((st = check_rope_table(p, d)) != GQA_OK) return st;
   if (N < 0) return GQA_EINVAL;
   if (N == 0) return GQA_OK;
   if (!tensor_ok(q) || !tensor_ok(q_out)) return GQA_EINVAL;

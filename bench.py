@@ -48,6 +48,7 @@ WORKLOADS = ("default", "tiny_f32", "prefill_4k", "varlen", "decode", "long_g4",
              "long_window", "long_blocks", "chunked", "decode_loop", "copy_calibration")
 WINDOW = 512          # sliding-window workload: keys per query
 BLOCK_DENSITY = 0.1   # block-sparse workload: share of earlier 64-key blocks kept
+ROPE_ALPHA = {"linear": 4.0, "ntk": 8.0, "yarn": 1.0}  # --rope-scaling extension factors
 COPY_BYTES = 1 << 30  # bytes read (and written) per step of the copy calibration
 
 
@@ -117,7 +118,7 @@ def visible_pairs(lengths, window=0, block_mask=None):
 
 
 class Prefill:
-    def __init__(self, case, window=0, block_mask=None):
+    def __init__(self, case, window=0, block_mask=None, rope_inv_freq=None):
         import torch
         import attention_head_qk_amd as gqa
         sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -133,6 +134,7 @@ class Prefill:
         self.window = window
         self.block_mask = block_mask
         self.masks = {}
+        self.rope = {} if rope_inv_freq is None else {"rope_inv_freq": rope_inv_freq}
         if window:
             self.masks["window"] = window
         if block_mask is not None:
@@ -141,7 +143,7 @@ class Prefill:
     def __call__(self, prof=None):
         c, dv = self.case, self.dev
         kw = dict(causal=c.causal, q_norm_w=dv["q_norm_w"], k_norm_w=dv["k_norm_w"], eps=c.eps,
-                  theta=c.theta, workspace=self.ws, prof=prof, **self.masks)
+                  theta=c.theta, workspace=self.ws, prof=prof, **self.masks, **self.rope)
         if c.dense:
             B, T = c.B, c.T_max
             return self.gqa.prefill(dv["q"].view(B, T, c.H, c.d), dv["k"].view(B, T, c.G, c.d),
@@ -398,6 +400,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=WORKLOADS, default="default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rope-scaling", choices=("none", "linear", "yarn", "ntk"), default="none",
+                    help="prefill workloads: RoPE through a scaled frequency table (linear x4; "
+                         "yarn from 32768 to 131072 training/inference tokens; ntk x8)")
     args = ap.parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -420,6 +425,12 @@ def main(argv=None):
     if args.workload == "chunked":
         pre = PrefillCached(W.prefill_chunked())
         log(f"bench: cached prefill inputs ready ({pre.case.name}, N={pre.case.N})")
+    elif args.rope_scaling != "none" and args.workload != "decode":
+        import attention_head_qk_amd as gqa
+        case = prefill_case(args.workload)
+        table = gqa.rope_freq_table(case.d, case.theta, args.rope_scaling, alpha=ROPE_ALPHA[args.rope_scaling],
+                                    train_len=32768, infer_len=131072)
+        pre = Prefill(case, rope_inv_freq=table)
     elif args.workload == "long_window":
         pre = Prefill(prefill_case(args.workload), window=WINDOW)
     elif args.workload == "long_blocks":
@@ -477,6 +488,8 @@ def main(argv=None):
             wname += f"_window{pre.window}"
         if getattr(pre, "block_mask", None) is not None:
             wname += "_blocks64"
+        if getattr(pre, "rope", None):
+            wname += "_rope_" + args.rope_scaling
         line.update({"value": round(tf_call, 3), "unit": "TFLOP/s",
                      "dtype": "f32" if c.dtype == W.F32 else "bf16"})
         line["roofline"] = {"bound": "mfma", "achieved": round(tf_kern, 3), "peak": peak,
@@ -492,6 +505,8 @@ def main(argv=None):
             cfg["prefill"].update(cache_lens=c.cache_lens.tolist(), max_seq=c.max_seq)
         if getattr(pre, "window", 0):
             cfg["prefill"]["window"] = pre.window
+        if getattr(pre, "rope", None):
+            cfg["prefill"]["rope_scaling"] = args.rope_scaling
         if getattr(pre, "block_mask", None) is not None:
             cfg["prefill"]["block_mask"] = {"block": 64, "kept": int(pre.block_mask.sum()),
                                             "density": BLOCK_DENSITY, "local": 1, "seed": 9}

@@ -38,7 +38,8 @@
  *     alias inputs.
  *   - Errors found on the host are returned at once and nothing is enqueued:
  *       GQA_EINVAL    null required pointer, negative size, H, G or d <= 0, H % G != 0,
- *                     a device pointer not 16-byte aligned, an int array not 4-byte aligned;
+ *                     a device pointer not 16-byte aligned, an int array not 4-byte aligned,
+ *                     a non-finite entry in rope_inv_freq;
  *       GQA_ENOTSUP   d not in {64, 128}, an unknown dtype, a bf16 prefill whose
  *                     T * G * d * 2 exceeds 2^31 - 1 bytes (one sequence's K rows) or
  *                     whose T * H / G exceeds 2^31 - 1 (its (position, head) columns), a
@@ -111,10 +112,17 @@ typedef struct gqa_params {
                                 / 64) for gqa_prefill_cached; one mask serves every sequence
                                 (indices inside the sequence).  NULL = no block mask        */
   int block_mask_words;      /* words per block_mask row, >= ceil(ceil(T_keys / 64) / 32)   */
+  const double *rope_inv_freq; /* optional HOST array of the d/2 RoPE frequencies omega_j
+                                (a scaled variant: linear interpolation, the architecture
+                                article's YaRN formula (3.4.2), an NTK base change...); read
+                                during the call (a decode graph keeps the values it saw at
+                                creation).  When set, RoPE is applied with it and rope_theta
+                                is ignored.  NULL = omega_j = rope_theta^(-2j/d)            */
 } gqa_params;
 
 /* Fills p with defaults: bf16, no norm weights, eps 1e-6, theta 1e6, scale 1/sqrt(d),
- * dense, no workspace, default stream, no profiling events, no window, no block mask. */
+ * dense, no workspace, default stream, no profiling events, no window, no block mask, no
+ * frequency table. */
 void gqa_params_init(gqa_params *p);
 
 /* Prefill (prompt) attention with the QK prologue.

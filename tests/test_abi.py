@@ -78,6 +78,30 @@ def test_pack_block_mask_bits():
             assert bit == (1 if kb < 70 and m[qb, kb] else 0)
 
 
+def test_rope_table_checked_before_launch():
+    bad = (ctypes.c_double * 64)(*([1.0] * 63 + [float("nan")]))
+    good = (ctypes.c_double * 64)(*([0.5] * 64))
+    short_ok = (ctypes.c_double * 32)(*([0.5] * 31 + [float("inf")]))  # d = 64 reads 32
+    assert _prefill(rope_inv_freq=ctypes.cast(bad, ctypes.POINTER(ctypes.c_double))) == _lib.GQA_EINVAL
+    assert _decode(rope_inv_freq=ctypes.cast(bad, ctypes.POINTER(ctypes.c_double))) == _lib.GQA_EINVAL
+    assert _prefill(rope_inv_freq=ctypes.cast(good, ctypes.POINTER(ctypes.c_double)), B=0) == _lib.GQA_OK
+    assert _prefill(d=64, rope_inv_freq=ctypes.cast(short_ok, ctypes.POINTER(ctypes.c_double))) == _lib.GQA_EINVAL
+
+
+def test_rope_freq_table_matches_the_oracle_tables():
+    import numpy as np
+    from attention_head_qk_amd import rope_freq_table
+    from oracle import gqa_oracle as O
+    for d in (64, 128):
+        assert np.allclose(rope_freq_table(d, 1e6), O.rope_inv_freq(d, 1e6), rtol=1e-14)
+        assert np.allclose(rope_freq_table(d, 1e6, "linear", alpha=4.0),
+                           O.inv_freq_linear(d, 1e6, 4.0), rtol=1e-14)
+        assert np.allclose(rope_freq_table(d, 1e6, "yarn", train_len=32768, infer_len=131072),
+                           O.inv_freq_yarn_page(d, 1e6, 32768, 131072), rtol=1e-12, atol=1e-300)
+        assert np.allclose(rope_freq_table(d, 1e6, "ntk", alpha=4.0),
+                           O.rope_inv_freq(d, O.ntk_theta(1e6, 4.0, d)), rtol=1e-12)
+
+
 def test_status_strings():
     for code, tag in [(0, "GQA_OK"), (1, "GQA_EINVAL"), (2, "GQA_ENOTSUP"),
                       (3, "GQA_EWORKSPACE"), (4, "GQA_EHIP")]:

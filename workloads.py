@@ -340,6 +340,8 @@ class CachedPrefillCase:
     max_seq: int
 
     def __getattr__(self, name):
+        if "new" not in self.__dict__:  # during copying, before the fields exist
+            raise AttributeError(name)
         return getattr(self.__dict__["new"], name)
 
     def cache_rows(self, b: int):
