@@ -85,14 +85,16 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int NMT = D / 32;              // 32-row tiles of O^T
   constexpr int KBYTES = KT * D * 2;       // one K tile
   constexpr int VBYTES = D * KT * 2;       // one V^T tile
-  constexpr int BUFBYTES = KBYTES + VBYTES;
   constexpr int KDMA = KBYTES / 1024 / 4;  // 1 KB DMA instructions per wave per K tile
   constexpr int KROWS_DMA = 1024 / (D * 2);  // K rows per DMA instruction
-  // The two buffers (K tile then V tile each) are separate LDS objects, so the compiler can
-  // tell that the DMA into one never feeds reads of the other and keeps its waits exact.
-  __shared__ __attribute__((aligned(16))) char smem0[BUFBYTES];
-  __shared__ __attribute__((aligned(16))) char smem1[BUFBYTES];
-  auto lds_buf = [&](int BUF) -> char* { return BUF ? smem1 : smem0; };
+  // The four tile buffers (K and V, two of each) are separate LDS objects, so the compiler can
+  // tell that the DMA into one never feeds reads of another and keeps its waits exact.
+  __shared__ __attribute__((aligned(16))) char kbuf0[KBYTES];
+  __shared__ __attribute__((aligned(16))) char kbuf1[KBYTES];
+  __shared__ __attribute__((aligned(16))) char vbuf0[VBYTES];
+  __shared__ __attribute__((aligned(16))) char vbuf1[VBYTES];
+  auto k_lds = [&](int BUF) -> char* { return BUF ? kbuf1 : kbuf0; };
+  auto v_lds = [&](int BUF) -> char* { return BUF ? vbuf1 : vbuf0; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -244,8 +246,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   // tiles, so the start matters; elsewhere the extra barrier and code cost more than the
   // trigonometry saved.
   const int npos = p_hi - p_lo + 1;
-  const bool rope_tab = MASK != 0 && a.use_rope && h >= 4 && npos * (D / 2) * 8 <= BUFBYTES;
-  f32x2_t* const tab = reinterpret_cast<f32x2_t*>(smem1);
+  const bool rope_tab = MASK != 0 && a.use_rope && h >= 4 && npos * (D / 2) * 8 <= KBYTES;
+  f32x2_t* const tab = reinterpret_cast<f32x2_t*>(kbuf1);
   auto build_rope_table = [&]() {
     for (int e = tid; e < npos * (D / 2); e += 256) {
       const int p = p_lo + e / (D / 2), j = e % (D / 2);
@@ -350,7 +352,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     const int cl = 2 * ((lane >> 4) & 1) + ((s16 & 3) >> 1);
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt)
-      v_roff[mt] = KBYTES + row * D * 2 + (((4 * mt + cl) ^ v_swz<D>(row)) * 16) + 8 * (s16 & 1);
+      v_roff[mt] = row * D * 2 + (((4 * mt + cl) ^ v_swz<D>(row)) * 16) + 8 * (s16 & 1);
   }
 
   // The buffer index is always a literal at the call sites, so after inlining every LDS
@@ -359,14 +361,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     const int soff = t * KT * row_bytes;
 #pragma unroll
     for (int i = 0; i < KDMA; ++i)
-      dma16(krs, lds_buf(BUF) + (i * 4 + wave) * 1024, k_voff,
+      dma16(krs, k_lds(BUF) + (i * 4 + wave) * 1024, k_voff,
             soff + i * 4 * KROWS_DMA * row_bytes);
   };
   auto issue_v = [&](int BUF, int t) {  // V tile t -> LDS buffer BUF (DMA)
     const int soff = t * KT * row_bytes;
 #pragma unroll
     for (int i = 0; i < KDMA; ++i)
-      dma16(vrs, lds_buf(BUF) + KBYTES + (i * 4 + wave) * 1024, vd_voff,
+      dma16(vrs, v_lds(BUF) + (i * 4 + wave) * 1024, vd_voff,
             soff + i * 4 * KROWS_DMA * row_bytes);
   };
 
@@ -382,7 +384,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   // against ~32 between independent issues), so the d-sum of each block is split in two
   // halves: four independent accumulators, added at the end.
   auto s_product = [&](int BUF, f32x16_t (&s)[2]) {
-    const char* sb = lds_buf(BUF);
+    const char* sb = k_lds(BUF);
     constexpr int HS = NST / 2;
     f32x16_t s4[2][2];
 #pragma unroll
@@ -481,7 +483,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   // ---- O^T += V^T P^T from LDS buffer BUF: round (kb, hf) issues one MFMA on each of the
   // NMT accumulators (independent chains), its V^T fragments read a round ahead
   auto pv_product = [&](int BUF, const uint32_t (&pk)[2][8]) {
-    const char* sb = lds_buf(BUF);
+    const char* sb = v_lds(BUF);
     bf16x8_t pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -548,9 +550,70 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     __syncthreads();
   };
 
+  // ---- software-pipelined step of the unmasked variant: S^T of tile t+1 runs on the matrix
+  // cores while the VALU does the softmax of tile t (one round of two MFMAs per slice of the
+  // probabilities), then O^T += V^T P^T of tile t. K runs one tile ahead of V: at step t,
+  // K(t+1) and V(t) are in LDS, K(t+2) and V(t+1) are in flight. sc holds S^T of tile t.
+  // (The products and the softmax are independent within a step. Pinning them together
+  // instruction by instruction needs more than 256 VGPRs and spills; left to itself the
+  // compiler groups the MFMAs ahead of the exponentials. Four accumulator chains for S^T
+  // here measured no better than two.)
+  constexpr int PPR = 16 / NST;  // probability pairs per lane per S round
+  auto pstep = [&](int P, int t, f32x16_t (&sc)[2]) {
+    const int tk = t + 2 < ntiles ? t + 2 : ntiles - 1;
+    const int tv = t + 1 < ntiles ? t + 1 : ntiles - 1;
+    issue_k(P, tk);      // K(t+2) -> kbuf P (K(t) was consumed by the previous step)
+    issue_v(1 - P, tv);  // V(t+1) -> vbuf 1-P
+    mask_tile(sc, t);
+    // S^T of tile t+1 from K(t+1) in two accumulator chains, in rounds that each also take
+    // a slice of tile t's probabilities
+    const char* kb = k_lds(1 - P);
+    f32x16_t sn[2] = {f32x16_t{}, f32x16_t{}};
+    uint32_t pk[2][8];
+    float ls4[4] = {0.f, 0.f, 0.f, 0.f};
+    u32x4_t kf[2][2];
+    auto kload = [&](int r, u32x4_t (&f)[2]) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        f[mt] = *reinterpret_cast<const u32x4_t*>(kb + k_roff[r] + mt * 32 * D * 2);
+    };
+    kload(0, kf[0]);
+#pragma unroll
+    for (int r = 0; r < NST; ++r) {
+      if (r + 1 < NST) kload(r + 1, kf[(r + 1) & 1]);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) sn[mt] = mfma32(as_bf16x8(kf[r & 1][mt]), qf[r], sn[mt]);
+#pragma unroll
+      for (int q = 0; q < PPR; ++q) {
+        const int pair = r * PPR + q, kk = pair >> 3, j = pair & 7;
+        f32x2_t pp = {__builtin_amdgcn_exp2f(sc[kk][2 * j]), __builtin_amdgcn_exp2f(sc[kk][2 * j + 1])};
+        const bf16x2_t pb2 = __builtin_convertvector(pp, bf16x2_t);
+        pk[kk][j] = __builtin_bit_cast(uint32_t, pb2);
+        ls4[j & 3] = __builtin_amdgcn_fdot2_f32_bf16(pb2, one2, ls4[j & 3], false);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float ls = (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
+    const float lt = l_run + ls;
+    bool exact = shifted || __any(!(ls <= 0x1p32f));
+    if (!exact && __any(!(lt >= 0x1p-100f))) exact = __any(!(lt + xor_shfl(lt, 32) >= 0x1p-100f));
+    if (exact) {
+      rescale(sc);
+      ls = probs(sc, pk, true);
+      shifted = true;
+    }
+    l_run += ls;
+    pv_product(P, pk);  // V(t) from vbuf P
+    sc[0] = sn[0];
+    sc[1] = sn[1];
+    wait_vmem();
+    __syncthreads();
+  };
+
   if constexpr (MASK == 0) {
     issue_k(0, 0);
     issue_v(0, 0);
+    issue_k(1, ntiles > 1 ? 1 : 0);
     if (rope_tab) {
       build_rope_table();
       __syncthreads();
@@ -558,12 +621,15 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     make_q();
     wait_vmem();
     __syncthreads();
+    f32x16_t sc[2];
+    s_product(0, sc);  // S^T of tile 0
+    __syncthreads();   // kbuf 0 is refilled by the first step
     int t = 0;
     for (; t + 1 < ntiles; t += 2) {
-      step(0, t, t + 1);
-      step(1, t + 1, t + 2 < ntiles ? t + 2 : t + 1);
+      pstep(0, t, sc);
+      pstep(1, t + 1, sc);
     }
-    if (t < ntiles) step(0, t, t);
+    if (t < ntiles) pstep(0, t, sc);
   } else {
     // visible tiles only; past the last one the loads repeat it (same instruction stream)
     int t = (MASK & 2) ? next_tile(t_first - 1) : t_first;

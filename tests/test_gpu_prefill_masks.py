@@ -109,16 +109,20 @@ def test_cached_prefill_with_masks():
 
 
 def test_wide_masks_change_no_bit():
-    # a window of at least the sequence, or a layout with every block kept, visits the same
-    # tiles in the same order as the plain kernel: the outputs are bit-identical
+    # a window of at least the sequence and a layout with every block kept visit the same
+    # tiles in the same order: the masked variants agree bit for bit with each other, and
+    # with the plain kernel up to the order of its score sums (the plain kernel runs its
+    # score product one tile ahead in two accumulator chains, the masked ones in four)
     case = W.make_prefill("wide", 190, lengths=[700], H=16, G=8)
     dev = device_prefill_inputs(case)
     say("prefill wide masks vs plain")
     plain = run_prefill(case, dev=dev)
     full = np.ones((_nb(700), _nb(700)), dtype=bool)
-    assert torch.equal(run_prefill(case, dev=dev, window=700), plain)
-    assert torch.equal(run_prefill(case, dev=dev, window=100000), plain)
-    assert torch.equal(run_prefill(case, dev=dev, block_mask=device_block_mask(full)), plain)
+    win = run_prefill(case, dev=dev, window=700)
+    assert torch.equal(run_prefill(case, dev=dev, window=100000), win)
+    assert torch.equal(run_prefill(case, dev=dev, block_mask=device_block_mask(full)), win)
+    err = (win.float() - plain.float()).abs()
+    assert float(err.max()) <= 2e-2 and float(err.mean()) <= 1e-3
 
 
 @pytest.mark.parametrize("sign", ["neg", "mixed"])
