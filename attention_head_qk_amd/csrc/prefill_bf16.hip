@@ -102,6 +102,19 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   const int l32 = lane & 31;
   const int grp = lane >> 5;
 
+  // ---- RoPE frequencies: each wave keeps its own copy in LDS, written and read by that wave
+  // only (so no barrier), filled just before the first Q row is rotated. Its global load is
+  // the first of the kernel, so waiting for it never includes the Q rows or the K/V tiles
+  // issued later (read lane by lane from the kernel argument inside the rotation, they cost
+  // one memory round trip per 16-element step).
+  __shared__ double s_omega[4][D / 2];
+  const double om_in = lane < D / 2 ? a.omega[lane] : 0.0;
+  auto fill_omega = [&]() {
+    if (lane < D / 2) s_omega[wave][lane] = om_in;
+    __builtin_amdgcn_wave_barrier();
+  };
+  const double* const om = s_omega[wave];
+
   // ---- block -> (sequence, group, column block). Heaviest first; with zigzag the second
   // half of the grid runs lightest first instead, so that block ids i and i + grid/2, which
   // the dispatcher places on the same CU when the whole grid is resident at once, carry
@@ -253,7 +266,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
       const int p = p_lo + e / (D / 2), j = e % (D / 2);
       const int pos = a.positions ? a.positions[seq0 + p] : past + p;
       float c, sn;
-      rope_cos_sin<true>((double)pos * a.omega[j], c, sn);
+      rope_cos_sin<true>((double)pos * om[j], c, sn);
       tab[e] = f32x2_t{c, sn};
     }
   };
@@ -299,7 +312,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
             c = cs[0];
             sn = cs[1];
           } else {
-            rope_cos_sin<true>((double)pos * a.omega[8 * st + 4 * grp + m], c, sn);
+            rope_cos_sin<true>((double)pos * om[8 * st + 4 * grp + m], c, sn);
           }
           // explicit FMAs: every kernel variant rounds the rotation the same way
           const float x0 = x[2 * m], x1 = x[2 * m + 1];
@@ -614,6 +627,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     issue_k(0, 0);
     issue_v(0, 0);
     issue_k(1, ntiles > 1 ? 1 : 0);
+    fill_omega();
     if (rope_tab) {
       build_rope_table();
       __syncthreads();
@@ -635,6 +649,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     int t = (MASK & 2) ? next_tile(t_first - 1) : t_first;
     issue_k(0, t);
     issue_v(0, t);
+    fill_omega();
     if (rope_tab) {
       build_rope_table();
       __syncthreads();

@@ -89,6 +89,26 @@ def test_dense_batches_full(lengths, H, G, d):
     check(got, oracle_prefill(case), W.BF16, case.name)
 
 
+# more dense causal grids of about one round of workgroups, every output element
+ONE_ROUND = [
+    ([1024], 16, 8, 128),
+    ([1000], 8, 8, 128),            # h = 1: a column block spans two key tiles of positions
+    ([2048], 32, 4, 128),           # h = 8, G = 4
+    ([3000], 32, 8, 64),            # d = 64, h = 4, ragged last tile
+    ([700, 700, 700], 16, 8, 128),  # a dense batch of three
+]
+
+
+@pytest.mark.parametrize("lengths,H,G,d", ONE_ROUND)
+def test_one_round_grids_full(lengths, H, G, d):
+    case = W.make_prefill(f"round_{lengths}_{H}_{G}_{d}", 61 + H + G + d, lengths=lengths,
+                          H=H, G=G, d=d)
+    assert case.dense
+    say("prefill", case.name)
+    got = to_f64(run_prefill(case))
+    check(got, oracle_prefill(case), W.BF16, case.name)
+
+
 @pytest.mark.parametrize("lengths,H,G,d,causal", [([150], 16, 8, 64, True), ([70, 0, 33], 12, 4, 128, True),
                                                   ([100], 8, 2, 128, False)])
 def test_small_shapes_f32(lengths, H, G, d, causal):
