@@ -148,6 +148,7 @@ struct PrologueArgs {
   int B, T, H, G;
   int max_seq;
   int use_rope;
+  int slot0;          // first token slot of this launch (set by the launcher)
   double omega[kMaxHalfD];  // theta^(-2j/d), computed on the host in fp64
 };
 

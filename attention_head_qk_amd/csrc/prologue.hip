@@ -12,6 +12,8 @@
 // them with DPP row permutes, and each lane evaluates its own four angles (cheap next to the
 // row's HBM traffic; rope_cos_sin gives the precision). With q null (the bf16 prefill, whose
 // attention kernel prepares Q itself) only K rows are processed.
+#include <algorithm>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -42,63 +44,81 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(PrologueArgs a) {
   constexpr int LPR = D / 8;  // lanes per head row (8 elements = one 16-byte bf16 chunk each)
   const int nq = a.q ? a.H : 0, nk = a.k ? a.G : 0;
   const int rows_per_token = nq + nk + ((a.decode && a.v) ? a.G : 0);
-  const long item = (long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;  // (token slot, row)
+  // (token slot, row) of this lane's row; the launcher keeps slots * rows below 2^31
+  const unsigned item = blockIdx.x * (256u / LPR) + threadIdx.x / LPR;
   const int ch = threadIdx.x % LPR;
   const int e0 = ch * 8;
-  const int slot = (int)(item / rows_per_token);
-  const int r = (int)(item % rows_per_token);
+  const int slot = a.slot0 + (int)(item / (unsigned)rows_per_token);
+  const int r = (int)(item % (unsigned)rows_per_token);
+  const bool is_q = r < nq, is_k = !is_q && r < nq + nk;
 
-  // ---- the token this row belongs to, its RoPE position, and the row's source/destination
+  // ---- the token this row belongs to. Every load of the row (data, gamma, position, the
+  // sequence's length, the four frequencies) is issued before the first wait: addresses of
+  // lanes past the end point at a valid row and their values are discarded. Only packed
+  // sequences need one load (cu_seqlens) before the row's address is known.
   bool active;
-  long tok = 0;        // token index of the source rows
-  long k_tok_out = 0;  // destination token row for K / V
-  int pos = 0;
+  int tok;         // token index of the source rows
+  int b = 0, t = 0;
   if (a.decode != 1) {
-    const int b = slot / a.T, t = slot % a.T;
+    b = slot / a.T;
+    t = slot - b * a.T;
     active = b < a.B;
-    if (active && a.cu_seqlens) {
-      const int s0 = a.cu_seqlens[b];
-      active = t < a.cu_seqlens[b + 1] - s0;
-      tok = s0 + t;
-    } else {
-      tok = slot;
-    }
-    if (active) pos = a.positions ? a.positions[tok] : t;
-    k_tok_out = tok;
-    if (a.decode == 2 && active) {
-      // cached prefill: the token follows the sequence's cached rows; its K/V go to slot
-      // past + t of the cache (rows that would not fit are not written)
-      const int past = max(0, min(a.seq_lens[b], a.max_seq));
-      if (!a.positions) pos = past + t;
-      k_tok_out = (long)b * a.max_seq + past + t;
-      if (r >= nq && past + t >= a.max_seq) active = false;
+    tok = active ? slot : 0;
+    if (a.cu_seqlens) {
+      const int bb = active ? b : 0;
+      const int s0 = a.cu_seqlens[bb];
+      active = active && t < a.cu_seqlens[bb + 1] - s0;
+      tok = active ? s0 + t : 0;
     }
   } else {
+    b = slot;
     active = slot < a.B;
-    const int L = active ? a.seq_lens[slot] : 0;
-    if (active) pos = a.positions ? a.positions[slot] : (L > 0 ? L - 1 : 0);
-    tok = slot;
-    k_tok_out = (long)slot * a.max_seq + (L > 0 ? L - 1 : 0);
+    tok = active ? slot : 0;
+  }
+  const int bb = active ? b : 0;
+  const T* src;
+  if (is_q) src = reinterpret_cast<const T*>(a.q) + ((long)tok * a.H + r) * D;
+  else if (is_k) src = reinterpret_cast<const T*>(a.k) + ((long)tok * a.G + (r - nq)) * D;
+  else src = reinterpret_cast<const T*>(a.v) + ((long)tok * a.G + (r - nq - nk)) * D;
+  const void* gam = is_q ? a.gq : (is_k ? a.gk : nullptr);
+  const T* gsrc = gam ? reinterpret_cast<const T*>(gam) : src;
+  const int32_t* pp = a.positions ? a.positions + tok : reinterpret_cast<const int32_t*>(src);
+  const int32_t* lp = (a.decode && a.seq_lens) ? a.seq_lens + bb : reinterpret_cast<const int32_t*>(src);
+  float x[8], gw[8];
+  load8(src + e0, x);
+  load8(gsrc + e0, gw);
+  const int pos_in = *pp;
+  const int len_in = *lp;
+  double om[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) om[m] = a.omega[4 * ch + m];
+
+  // ---- the RoPE position and the destination row (K / V rows of decode and cached prefill
+  // go to the cache)
+  int pos;
+  long k_tok_out;  // destination token row for K / V
+  if (a.decode == 0) {
+    pos = a.positions ? pos_in : t;
+    k_tok_out = tok;
+  } else if (a.decode == 2) {
+    // cached prefill: the token follows the sequence's cached rows; its K/V go to slot
+    // past + t of the cache (rows that would not fit are not written)
+    const int past = max(0, min(len_in, a.max_seq));
+    pos = a.positions ? pos_in : past + t;
+    k_tok_out = (long)bb * a.max_seq + past + t;
+    if (r >= nq && past + t >= a.max_seq) active = false;
+  } else {
+    const int L = len_in;
+    pos = a.positions ? pos_in : (L > 0 ? L - 1 : 0);
+    k_tok_out = (long)bb * a.max_seq + (L > 0 ? L - 1 : 0);
     if (r >= a.H && L == 0) active = false;  // nothing to append to an empty sequence
   }
-  const bool is_q = r < nq, is_k = !is_q && r < nq + nk;
-  const T* src;
   T* dst;
-  if (is_q) {
-    src = reinterpret_cast<const T*>(a.q) + (tok * a.H + r) * (long)D;
-    dst = reinterpret_cast<T*>(a.q_out) + (tok * a.H + r) * (long)D;
-  } else if (is_k) {
-    src = reinterpret_cast<const T*>(a.k) + (tok * a.G + (r - nq)) * (long)D;
-    dst = reinterpret_cast<T*>(a.k_out) + (k_tok_out * a.G + (r - nq)) * (long)D;
-  } else {
-    src = reinterpret_cast<const T*>(a.v) + (tok * a.G + (r - nq - nk)) * (long)D;
-    dst = reinterpret_cast<T*>(a.v_out) + (k_tok_out * a.G + (r - nq - nk)) * (long)D;
-  }
+  if (is_q) dst = reinterpret_cast<T*>(a.q_out) + ((long)tok * a.H + r) * D;
+  else if (is_k) dst = reinterpret_cast<T*>(a.k_out) + (k_tok_out * a.G + (r - nq)) * D;
+  else dst = reinterpret_cast<T*>(a.v_out) + (k_tok_out * a.G + (r - nq - nk)) * D;
 
-  float x[8];
-  if (active) {
-    load8(src + e0, x);
-  } else {
+  if (!active) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = 0.f;
   }
@@ -108,10 +128,7 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(PrologueArgs a) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
   ss = lane_group_sum<LPR>(ss);
-  const void* gam = is_q ? a.gq : (is_k ? a.gk : nullptr);
   if (gam) {
-    float gw[8];
-    load8(reinterpret_cast<const T*>(gam) + e0, gw);
     const float rinv = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = (x[i] * rinv) * gw[i];
@@ -120,7 +137,7 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(PrologueArgs a) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       float c, sn;
-      rope_cos_sin<sizeof(T) == 2>((double)pos * a.omega[4 * ch + m], c, sn);
+      rope_cos_sin<sizeof(T) == 2>((double)pos * om[m], c, sn);
       const float x0 = x[2 * m], x1 = x[2 * m + 1];
       x[2 * m] = x0 * c - x1 * sn;
       x[2 * m + 1] = x0 * sn + x1 * c;
@@ -132,11 +149,20 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(PrologueArgs a) {
 template <typename T, int D>
 static hipError_t launch_prologue_t(const PrologueArgs& a, int slots, hipStream_t s) {
   constexpr int ROWS_PER_BLOCK = 256 / (D / 8);
-  const long rows = (long)slots * ((a.q ? a.H : 0) + (a.k ? a.G : 0) + ((a.decode && a.v) ? a.G : 0));
-  const long grid = (rows + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((qk_norm_rope_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, s, a);
-  return hipGetLastError();
+  const long rpt = (a.q ? a.H : 0) + (a.k ? a.G : 0) + ((a.decode && a.v) ? a.G : 0);
+  if (rpt == 0) return hipSuccess;
+  // launches of at most 2^30 rows, so the kernel's row index stays 32-bit
+  const long per = std::max(1L, (1L << 30) / rpt);
+  for (long s0 = 0; s0 < slots; s0 += per) {
+    PrologueArgs c = a;
+    c.slot0 = (int)s0;
+    const long rows = std::min(per, (long)slots - s0) * rpt;
+    const long grid = (rows + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
+    hipLaunchKernelGGL((qk_norm_rope_kernel<T, D>), dim3((unsigned)grid), dim3(256), 0, s, c);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_prologue(const PrologueArgs& a, int slots, int d, bool bf16, hipStream_t s) {
