@@ -167,6 +167,7 @@ struct PrefillArgs {
   int causal;
   int n_blk;          // column blocks of the longest sequence
   int zigzag;         // 1: pair heavy and light blocks (see the prefill kernel)
+  int rank_chunk;     // bf16 kernel: consecutive ranks of one sequence before the next one
   const int32_t* cache_lens;  // bf16 kernel, cached prefill: earlier tokens per sequence in
                               // the cache; kt / v are then caches [B, max_seq, G, D]
   int max_seq;

@@ -342,6 +342,10 @@ gqa_status gqa_prefill(const void* q, const void* k, const void* v, const int32_
     const long grid = (long)B * G * fa.n_blk;
     fa.zigzag = (causal && !p->cu_seqlens && grid <= 4L * n_cu) ? 1 : 0;
   }
+  // several sequences: runs of 32 ranks per sequence keep fewer sequences' K/V in each
+  // XCD's L2 at a time (measured: varlen 8 x [512, 8192] 1.68 -> 1.46 ms, chunked 1.63 ->
+  // 1.54 ms)
+  fa.rank_chunk = (fa.zigzag || B == 1) ? 1 : 32;
   fa.scale = eff_scale(p, d);
   fa.scale_log2e = (float)((double)fa.scale * 1.4426950408889634074);
   if ((st = from_hip(mark(p->prof_start, stream))) != GQA_OK) return st;
@@ -417,6 +421,10 @@ gqa_status gqa_prefill_cached(const void* q, const void* k, const void* v, void*
   const int cpb = gqa::prefill_bf16_cols_per_block();
   fa.n_blk = (int)((cols + cpb - 1) / cpb);
   fa.zigzag = 0;
+  // several sequences: runs of 32 ranks per sequence keep fewer sequences' K/V in each
+  // XCD's L2 at a time (measured: varlen 8 x [512, 8192] 1.68 -> 1.46 ms, chunked 1.63 ->
+  // 1.54 ms)
+  fa.rank_chunk = (fa.zigzag || B == 1) ? 1 : 32;
   fa.scale = eff_scale(p, d);
   fa.scale_log2e = (float)((double)fa.scale * 1.4426950408889634074);
   if ((st = from_hip(mark(p->prof_start, stream))) != GQA_OK) return st;

@@ -119,11 +119,22 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   // half of the grid runs lightest first instead, so that block ids i and i + grid/2, which
   // the dispatcher places on the same CU when the whole grid is resident at once, carry
   // complementary causal work (n_blk - r and r + 1 tiles).
+  // With rank_chunk > 1 the ranks go in chunks: the B sequences take turns with runs of
+  // rank_chunk consecutive ranks each, so an XCD holds the K/V of fewer sequences at once.
   const int id = blockIdx.x;
   const int g = id % a.G;
   const int rest = id / a.G;
-  const int b = rest % a.B;
-  const int r = rest / a.B;
+  int b, r;
+  if (a.rank_chunk > 1) {
+    const int chunk = rest / (a.B * a.rank_chunk);
+    const int w = rest - chunk * a.B * a.rank_chunk;
+    const int rb = min(a.rank_chunk, a.n_blk - chunk * a.rank_chunk);
+    b = w / rb;
+    r = chunk * a.rank_chunk + (w - b * rb);
+  } else {
+    b = rest % a.B;
+    r = rest / a.B;
+  }
   const int half_r = (a.n_blk + 1) / 2;
   const int blk = (a.zigzag && r >= half_r) ? r - half_r : a.n_blk - 1 - r;
   int seq0, Tb;
