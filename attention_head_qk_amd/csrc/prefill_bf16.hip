@@ -42,7 +42,8 @@
 //   rounds, heavy and light blocks are paired instead (zigzag). The group index is the
 //   fastest-varying part of the block id, which keeps the blocks of one KV group on the same
 //   XCD (blocks are dealt round-robin over the 8 XCDs) when G is a multiple of 8, so its K/V
-//   stay in that XCD's L2.
+//   stay in that XCD's L2; with several sequences the ranks go in runs of 32 per sequence, so
+//   an XCD streams few sequences' K/V at a time.
 #include "device_common.h"
 #include "kernels.h"
 
