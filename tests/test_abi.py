@@ -287,3 +287,23 @@ def test_qk_norm_rope_rejects_before_launch():
     assert f(A, None, None, A, None, -1, 4, 2, 128, ctypes.byref(p)) == _lib.GQA_EINVAL
     assert f(A, None, None, A, None, 0, 4, 2, 128, ctypes.byref(p)) == _lib.GQA_OK
     assert f(A, None, None, A, None, 4, 4, 2, 128, None) == _lib.GQA_EINVAL
+
+
+def test_c_client_compiles_and_links():
+    # the header is plain C: tests/c_abi/client.c (the GPU test's C client) builds with gcc
+    # against include/gqa.h and links libgqa.so and the HIP runtime
+    import shutil
+    import subprocess
+    import tempfile
+    cc = shutil.which("gcc")
+    if cc is None:
+        pytest.skip("no gcc")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    pkg = os.path.join(root, "attention_head_qk_amd")
+    with tempfile.TemporaryDirectory() as t:
+        r = subprocess.run([cc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                            "-I", os.path.join(root, "include"), "-I", "/opt/rocm/include",
+                            os.path.join(root, "tests", "c_abi", "client.c"), "-L", pkg, "-lgqa",
+                            "-L", "/opt/rocm/lib", "-lamdhip64", "-o", os.path.join(t, "client")],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
