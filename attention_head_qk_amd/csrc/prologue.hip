@@ -151,8 +151,9 @@ static hipError_t launch_prologue_t(const PrologueArgs& a, int slots, hipStream_
   constexpr int ROWS_PER_BLOCK = 256 / (D / 8);
   const long rpt = (a.q ? a.H : 0) + (a.k ? a.G : 0) + ((a.decode && a.v) ? a.G : 0);
   if (rpt == 0) return hipSuccess;
-  // launches of at most 2^30 rows, so the kernel's row index stays 32-bit
-  const long per = std::max(1L, (1L << 30) / rpt);
+  // launches of at most 2^22 rows (2^18 workgroups), so the kernel's row index stays
+  // 32-bit with room to spare; inputs that large amortise the extra launches
+  const long per = std::max(1L, (1L << 22) / rpt);
   for (long s0 = 0; s0 < slots; s0 += per) {
     PrologueArgs c = a;
     c.slot0 = (int)s0;

@@ -61,3 +61,31 @@ def test_prologue_without_norm_or_rope(dtype):
     ar = np.arange(33)
     _cmp(to_f64(qo), O.rope(W.to_f64(q, dtype), ar, 1e6), dtype, "q")
     _cmp(to_f64(ko), O.rope(W.to_f64(k, dtype), ar, 1e6), dtype, "k")
+
+
+def test_prologue_in_several_launches():
+    # more than 2^22 (token, head) rows: the launcher splits the pass into launches of whole
+    # token slots; rows on both sides of each launch boundary are checked against the oracle
+    import torch
+    import attention_head_qk_amd as gqa
+    N, H, G, d = 480_000, 16, 2, 128   # 8.6M rows: two launches of 233,016 tokens and a rest
+    g = torch.Generator(device="cuda").manual_seed(501)
+    q = torch.randn((N, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((N, G, d), generator=g, device="cuda").to(torch.bfloat16)
+    gq = (torch.rand((d,), generator=g, device="cuda") + 0.5).to(torch.bfloat16)
+    gk = (torch.rand((d,), generator=g, device="cuda") + 0.5).to(torch.bfloat16)
+    say("prologue over 5.4M rows")
+    qo, ko = gqa.qk_norm_rope(q, k, None, q_norm_w=gq, k_norm_w=gk)
+    torch.cuda.synchronize()
+    per = (1 << 22) // (H + G)
+    toks = sorted({0, 1, per - 1, per, per + 1, 2 * per - 1, 2 * per, N - 1, 12345, 250_001})
+    assert 2 * per < N and all(0 <= t < N for t in toks)  # every sampled token exists
+    idx = torch.tensor(toks, device="cuda")
+
+    def host(t):
+        return t.index_select(0, idx).float().cpu().numpy().astype(np.float64)
+    qt, kt = O.qk_norm_rope(host(q), host(k), np.array(toks, np.int32),
+                            gq.float().cpu().numpy().astype(np.float64),
+                            gk.float().cpu().numpy().astype(np.float64), 1e-6, 1e6)
+    for got, want in ((host(qo), qt), (host(ko), kt)):
+        assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 1e-6)
