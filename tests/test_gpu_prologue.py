@@ -74,7 +74,7 @@ def test_prologue_in_several_launches():
     k = torch.randn((N, G, d), generator=g, device="cuda").to(torch.bfloat16)
     gq = (torch.rand((d,), generator=g, device="cuda") + 0.5).to(torch.bfloat16)
     gk = (torch.rand((d,), generator=g, device="cuda") + 0.5).to(torch.bfloat16)
-    say("prologue over 5.4M rows")
+    say("prologue over 8.6M rows in three launches")
     qo, ko = gqa.qk_norm_rope(q, k, None, q_norm_w=gq, k_norm_w=gk)
     torch.cuda.synchronize()
     per = (1 << 22) // (H + G)
