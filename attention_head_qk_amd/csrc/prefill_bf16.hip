@@ -506,7 +506,11 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   };
 
   // ---- O^T += V^T P^T from LDS buffer BUF: round (kb, hf) issues one MFMA on each of the
-  // NMT accumulators (independent chains), its V^T fragments read a round ahead
+  // NMT accumulators (independent chains), its V^T fragments read a round ahead. The wave
+  // runs this all-MFMA stretch at raised issue priority, so that on a SIMD shared with a
+  // wave of the other workgroup its products go first whenever the matrix core is free and
+  // the other wave's exponentials fill the VALU slots between them (measured 1-2% faster on
+  // the dense, long and varlen workloads; the same raise on the S^T rounds was not).
   auto pv_product = [&](int BUF, const uint32_t (&pk)[2][8]) {
     const char* sb = v_lds(BUF);
     bf16x8_t pb[2][2];
@@ -525,6 +529,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
       }
     };
     load(0, vf[0]);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       if (r + 1 < 4) load(r + 1, vf[(r + 1) & 1]);
@@ -532,6 +537,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
       for (int mt = 0; mt < NMT; ++mt) o[mt] = mfma32(as_bf16x8(vf[r & 1][mt]), pb[r >> 1][r & 1], o[mt]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- pipeline: the K and V tiles of step t+1 are in flight (DMA into buffer 1-P) while tile
