@@ -121,8 +121,7 @@ class Prefill:
     def __init__(self, case, window=0, block_mask=None, rope_inv_freq=None):
         import torch
         import attention_head_qk_amd as gqa
-        sys.path.insert(0, os.path.join(ROOT, "tests"))
-        from _gpu import device_prefill_inputs
+        from workloads import device_prefill_inputs
         self.case = case
         self.dev = device_prefill_inputs(case)
         self.gqa = gqa
@@ -166,8 +165,7 @@ class PrefillCached:
 
     def __init__(self, case):
         import attention_head_qk_amd as gqa
-        sys.path.insert(0, os.path.join(ROOT, "tests"))
-        from _gpu import device_cached_inputs
+        from workloads import device_cached_inputs
         self.case = case
         self.dev = device_cached_inputs(case)
         self.gqa = gqa
@@ -190,8 +188,7 @@ class Decode:
     def __init__(self, case):
         import torch
         import attention_head_qk_amd as gqa
-        sys.path.insert(0, os.path.join(ROOT, "tests"))
-        from _gpu import device_decode_inputs
+        from workloads import device_decode_inputs
         self.case = case
         self.dev = device_decode_inputs(case)
         self.gqa = gqa
@@ -303,8 +300,7 @@ class DecodeLoop:
     def __init__(self, case):
         import attention_head_qk_amd as gqa
         import torch
-        sys.path.insert(0, os.path.join(ROOT, "tests"))
-        from _gpu import device_steps_inputs
+        from workloads import device_steps_inputs
         self.case = c = case
         dev = device_steps_inputs(case)
         self.gqa, self.dev = gqa, dev

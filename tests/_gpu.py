@@ -9,6 +9,8 @@ import numpy as np
 import torch
 
 import workloads as W
+from workloads import (device_cached_inputs, device_decode_inputs,  # noqa: F401
+                       device_prefill_inputs, device_steps_inputs, i32, to_dev)
 
 F32_MAX_ABS = 1e-5
 BF16_MAX_ABS = 2e-2
@@ -21,16 +23,8 @@ def say(*a):
     sys.stdout.flush()
 
 
-def to_dev(arr: np.ndarray, dtype: str) -> torch.Tensor:
-    if dtype == W.BF16:
-        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
-    else:
-        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
-    return t.cuda()
 
 
-def i32(arr) -> torch.Tensor:
-    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.int32)).cuda()
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:
@@ -48,11 +42,6 @@ def check(got: np.ndarray, want: np.ndarray, dtype: str, what: str = "") -> dict
     return stats
 
 
-def device_prefill_inputs(case: W.PrefillCase):
-    dt = case.dtype
-    return dict(q=to_dev(case.q, dt), k=to_dev(case.k, dt), v=to_dev(case.v, dt),
-                q_norm_w=to_dev(case.q_norm_w, dt), k_norm_w=to_dev(case.k_norm_w, dt),
-                positions=i32(case.positions), cu=i32(case.cu_seqlens))
 
 
 def run_prefill(case: W.PrefillCase, dev=None, packed=None, pass_positions=True, **kw):
@@ -113,24 +102,6 @@ def sample_rows(case: W.PrefillCase, n_random: int, seed: int = 0, tile: int = 6
     return np.array(sorted(rows), dtype=np.int64)
 
 
-def device_decode_inputs(case: W.DecodeCase, fill_invalid=None):
-    """Device tensors for a decode case; the cache is [B, max_seq, G, d] with only the first
-    seq_lens[b] rows of each sequence filled (the rest zero, or ``fill_invalid``)."""
-    dt = case.dtype
-    tdt = torch.bfloat16 if dt == W.BF16 else torch.float32
-    shape = (case.B, case.max_seq, case.G, case.d)
-    kc = torch.zeros(shape, dtype=tdt, device="cuda")
-    vc = torch.zeros(shape, dtype=tdt, device="cuda")
-    if fill_invalid is not None:
-        kc.fill_(fill_invalid)
-        vc.fill_(fill_invalid)
-    for b, k, v in case.iter_cache_rows():
-        L = k.shape[0]
-        kc[b, :L] = to_dev(k, dt)
-        vc[b, :L] = to_dev(v, dt)
-    return dict(q=to_dev(case.q, dt), k_cache=kc, v_cache=vc, seq_lens=i32(case.seq_lens),
-                k_new=to_dev(case.k_new, dt), v_new=to_dev(case.v_new, dt),
-                q_norm_w=to_dev(case.q_norm_w, dt), k_norm_w=to_dev(case.k_norm_w, dt))
 
 
 def run_decode(case: W.DecodeCase, dev, append=True, positions=None, **kw):
@@ -152,25 +123,6 @@ def oracle_decode_seq(case: W.DecodeCase, b: int, append=True, position=None):
                         v_new=case.f64("v_new")[b] if append else None)
 
 
-def device_cached_inputs(case: W.CachedPrefillCase, fill_invalid=None):
-    """Device tensors for a cached-prefill case: the new tokens (packed) and caches
-    [B, max_seq, G, d] holding cache_lens[b] rows per sequence (the rest zero, or
-    ``fill_invalid``)."""
-    dev = device_prefill_inputs(case.new)
-    shape = (case.B, case.max_seq, case.G, case.d)
-    kc = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
-    vc = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
-    if fill_invalid is not None:
-        kc.fill_(fill_invalid)
-        vc.fill_(fill_invalid)
-    for b in range(case.B):
-        k, v = case.cache_rows(b)
-        L = k.shape[0]
-        if L:
-            kc[b, :L] = to_dev(k, W.BF16)
-            vc[b, :L] = to_dev(v, W.BF16)
-    dev.update(k_cache=kc, v_cache=vc, cache_lens=i32(case.cache_lens))
-    return dev
 
 
 def run_prefill_cached(case: W.CachedPrefillCase, dev, packed=None, pass_positions=True, **kw):
@@ -208,26 +160,6 @@ def oracle_prefill_cached_seq(case: W.CachedPrefillCase, b: int, positions=None,
     return out, kc2[0], vc2[0]
 
 
-def device_steps_inputs(case: W.DecodeStepsCase, fill_invalid=None):
-    """Device tensors for a decode-loop case: per-step q [S, B, H, d], k / v [S, B, G, d],
-    caches [B, max_seq, G, d] holding cache_lens[b] rows (the rest zero or ``fill_invalid``),
-    and seq_lens = cache_lens."""
-    dt = case.dtype
-    tdt = torch.bfloat16 if dt == W.BF16 else torch.float32
-    shape = (case.B, case.max_seq, case.G, case.d)
-    kc = torch.zeros(shape, dtype=tdt, device="cuda")
-    vc = torch.zeros(shape, dtype=tdt, device="cuda")
-    if fill_invalid is not None:
-        kc.fill_(fill_invalid)
-        vc.fill_(fill_invalid)
-    for b in range(case.B):
-        k, v = case.cache_rows(b)
-        if k.shape[0]:
-            kc[b, :k.shape[0]] = to_dev(k, dt)
-            vc[b, :k.shape[0]] = to_dev(v, dt)
-    return dict(q=to_dev(case.q, dt), k=to_dev(case.k, dt), v=to_dev(case.v, dt), k_cache=kc,
-                v_cache=vc, seq_lens=i32(case.cache_lens), q_norm_w=to_dev(case.q_norm_w, dt),
-                k_norm_w=to_dev(case.k_norm_w, dt))
 
 
 def oracle_decode_steps(case: W.DecodeStepsCase):

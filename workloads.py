@@ -1,8 +1,9 @@
 """Seeded synthetic inputs for causal grouped-query attention (QK-RMSNorm + RoPE).
 
-This module only draws numbers and encodes them in the storage dtype. It holds none of the
-attention arithmetic, so both the fp64 CPU oracle (under ``oracle/``) and the HIP path can
-take their inputs from here without sharing any of the method's code.
+This module only draws numbers, encodes them in the storage dtype and (at the end) copies
+them into device tensors. It holds none of the attention arithmetic, so both the fp64 CPU
+oracle (under ``oracle/``) and the HIP path can take their inputs from here without sharing
+any of the method's code.
 
 Recipe (the pages measure nothing at the kernel level, so the inputs stand in for
 post-projection Q/K/V activations at Qwen3 head shapes):
@@ -423,3 +424,77 @@ def decode_loop():
     lens = rng.integers(256, 2048 + 1, size=16)
     return make_decode_steps("bf16_decode_loop_16x64_from_[256,2048]_H32_G8_d128", 8, lens, 64,
                              4096)
+
+
+# ----------------------------------------------------------------------------- device placement
+# Copies a case's stored arrays into device tensors (bit-exact: bf16 travels as its 16-bit
+# pattern). torch is imported here only, so the CPU oracle never needs it.
+def to_dev(arr: np.ndarray, dtype: str):
+    import torch
+    if dtype == BF16:
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.cuda()
+
+
+def i32(arr):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.int32)).cuda()
+
+
+def _device_caches(B, max_seq, G, d, dtype, rows, fill_invalid):
+    """K/V caches [B, max_seq, G, d]: each (b, k, v) of ``rows`` fills the first rows of
+    sequence b; the rest are zero, or ``fill_invalid``."""
+    import torch
+    tdt = torch.bfloat16 if dtype == BF16 else torch.float32
+    kc = torch.zeros((B, max_seq, G, d), dtype=tdt, device="cuda")
+    vc = torch.zeros((B, max_seq, G, d), dtype=tdt, device="cuda")
+    if fill_invalid is not None:
+        kc.fill_(fill_invalid)
+        vc.fill_(fill_invalid)
+    for b, k, v in rows:
+        L = k.shape[0]
+        if L:
+            kc[b, :L] = to_dev(k, dtype)
+            vc[b, :L] = to_dev(v, dtype)
+    return kc, vc
+
+
+def device_prefill_inputs(case: PrefillCase) -> dict:
+    dt = case.dtype
+    return dict(q=to_dev(case.q, dt), k=to_dev(case.k, dt), v=to_dev(case.v, dt),
+                q_norm_w=to_dev(case.q_norm_w, dt), k_norm_w=to_dev(case.k_norm_w, dt),
+                positions=i32(case.positions), cu=i32(case.cu_seqlens))
+
+
+def device_decode_inputs(case: DecodeCase, fill_invalid=None) -> dict:
+    """Device tensors for a decode case; the cache holds the first seq_lens[b] rows of each
+    sequence."""
+    dt = case.dtype
+    kc, vc = _device_caches(case.B, case.max_seq, case.G, case.d, dt, case.iter_cache_rows(),
+                            fill_invalid)
+    return dict(q=to_dev(case.q, dt), k_cache=kc, v_cache=vc, seq_lens=i32(case.seq_lens),
+                k_new=to_dev(case.k_new, dt), v_new=to_dev(case.v_new, dt),
+                q_norm_w=to_dev(case.q_norm_w, dt), k_norm_w=to_dev(case.k_norm_w, dt))
+
+
+def device_cached_inputs(case: CachedPrefillCase, fill_invalid=None) -> dict:
+    """Device tensors for a cached-prefill case: the new tokens (packed) and caches holding
+    cache_lens[b] rows per sequence."""
+    dev = device_prefill_inputs(case.new)
+    kc, vc = _device_caches(case.B, case.max_seq, case.G, case.d, BF16,
+                            ((b, *case.cache_rows(b)) for b in range(case.B)), fill_invalid)
+    dev.update(k_cache=kc, v_cache=vc, cache_lens=i32(case.cache_lens))
+    return dev
+
+
+def device_steps_inputs(case: DecodeStepsCase, fill_invalid=None) -> dict:
+    """Device tensors for a decode-loop case: per-step q [S, B, H, d], k / v [S, B, G, d],
+    caches holding cache_lens[b] rows, and seq_lens = cache_lens."""
+    dt = case.dtype
+    kc, vc = _device_caches(case.B, case.max_seq, case.G, case.d, dt,
+                            ((b, *case.cache_rows(b)) for b in range(case.B)), fill_invalid)
+    return dict(q=to_dev(case.q, dt), k=to_dev(case.k, dt), v=to_dev(case.v, dt), k_cache=kc,
+                v_cache=vc, seq_lens=i32(case.cache_lens), q_norm_w=to_dev(case.q_norm_w, dt),
+                k_norm_w=to_dev(case.k_norm_w, dt))
