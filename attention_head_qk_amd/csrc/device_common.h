@@ -97,9 +97,12 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // address is taken from the first lane, so it must be the same for the whole wave).
 // (A plain address-space cast keeps the pointer's provenance, so alias analysis can tell
 // which LDS array a DMA writes.)
+// POL is the instruction's cache-policy operand (0, or kNonTemporal).
+constexpr int kNonTemporal = 2;  // the "nt" bit: streamed data, not kept in the caches
+template <int POL = 0>
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, const char* lds, int voff, int soff) {
   typedef __attribute__((address_space(3))) void lds_void;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)const_cast<char*>(lds), 16, voff, soff, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)const_cast<char*>(lds), 16, voff, soff, 0, POL);
 }
 
 // cos and sin of the RoPE angle phi = pos * omega_j: the angle is reduced to revolutions in
@@ -190,6 +193,7 @@ struct DecodeArgs {
   void* out;          // [B, H, D]
   int B, H, G, h, max_seq, nsplit;
   int split;          // keys per split, a multiple of 128 (4 waves x 32 keys)
+  int stream_v;       // 1: V rows are read non-temporally (caches larger than the chip's caches)
   float scale_log2e;
 };
 

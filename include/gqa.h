@@ -171,6 +171,8 @@ gqa_status gqa_prefill_cached(const void *q, const void *k, const void *v, void 
  *     slot seq_lens[b]-1 first (so k_cache and v_cache are written only then).
  *   seq_lens: device [B], 0 <= seq_lens[b] <= max_seq, counting the new token.
  *   p->window and p->block_mask are not supported here (GQA_ENOTSUP when set).
+ *   When the two caches together exceed 512 MiB (2*B*max_seq*G*d*elem bytes) the bf16 pass
+ *   reads V with a non-temporal cache hint; the results are the same bits either way.
  *   Needs p->workspace of gqa_workspace_bytes(GQA_OP_DECODE, B, max_seq, H, G, d, dtype). */
 gqa_status gqa_decode(const void *q, void *k_cache, void *v_cache, const int32_t *seq_lens,
                       void *out, int B, int H, int G, int d, int max_seq,

@@ -40,7 +40,8 @@ def edge_lens(S):
                                    (6, 2, 64), (40, 1, 128)])
 def test_decode_edge_lengths(dtype, H, G, d, max_seq):
     # the split length follows the shape (1024, 512 and 256 all occur over these cases); the
-    # lengths sit on that split's edges
+    # lengths sit on that split's edges. At max_seq 24576 the bf16 caches of the G = 8 and
+    # G = 4 shapes exceed 512 MiB, so those cases take the pass that streams V non-temporally.
     import attention_head_qk_amd as gqa
     B = 13
     S = gqa.decode_split_keys(B, H, G, max_seq)
