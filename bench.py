@@ -26,8 +26,8 @@ timed region. Prints one JSON line:
   each step advances seq_lens on the device and decodes one token per sequence. value = GB/s
   of the step replayed as one HIP graph (gqa_decode_graph_*); the eager step (a torch add and
   gqa_decode) is reported beside it.
-* cpu_baseline: the fp64 CPU oracle timed on the host CPU of the same machine on a bounded sample of the
-  same prefill workload.
+* cpu_baseline: the fp64 CPU oracle timed on the host CPU of the same machine, on a bounded
+  sample of the same prefill workload.
 """
 from __future__ import annotations
 
