@@ -27,6 +27,10 @@ bool dtype_ok(int dtype) { return dtype == GQA_F32 || dtype == GQA_BF16; }
 // still spread over the chip. Only the host-visible sizes enter (seq_lens live on the device).
 constexpr long kDecodeMinBlocks = 2048;
 
+// Largest grid y or z dimension of a launch: the decode passes and the fp32 prefill put the
+// sequence index there.
+constexpr int kMaxGridYZ = 65535;
+
 // Caches whose K and V allocations together exceed this are streamed (V read non-temporally):
 // twice the 256 MB last-level cache, so a loop over a cache that fits keeps finding it there.
 // Measured: 64 sequences over a 8.6 GB allocation (5 GB read) 893 -> 826 us for the split
@@ -132,6 +136,7 @@ gqa_status decode_check(const void* q, void* k_cache, void* v_cache, const int32
   if (p->window != 0 || p->block_mask) return GQA_ENOTSUP;
   if (B == 0) return GQA_OK;
   if (max_seq == 0) return GQA_EINVAL;
+  if (B > kMaxGridYZ) return GQA_ENOTSUP;
   // one sequence's cache rows are addressed with 32-bit byte offsets, and the combine pass
   // merges at most kMaxCombineSplits splits per sequence
   if ((long long)max_seq * G * d * (long long)elem_size(p->dtype) > 0x7fffffffLL ||
@@ -282,6 +287,7 @@ gqa_status gqa_prefill(const void* q, const void* k, const void* v, const int32_
   if (p->dtype == GQA_BF16 && (long long)T * G * d * 2 > 0x7fffffffLL) return GQA_ENOTSUP;
   // the bf16 kernel numbers a sequence's (position, head) columns with 32-bit integers
   if (p->dtype == GQA_BF16 && (long long)T * (H / G) > 0x7fffffffLL) return GQA_ENOTSUP;
+  if (p->dtype == GQA_F32 && B > kMaxGridYZ) return GQA_ENOTSUP;
   if ((st = check_masks(p, causal, T)) != GQA_OK) return st;
   if (B == 0 || T == 0) return GQA_OK;
   if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(out)) return GQA_EINVAL;

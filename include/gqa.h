@@ -45,7 +45,8 @@
  *                     whose T * H / G exceeds 2^31 - 1 (its (position, head) columns), a
  *                     decode whose max_seq * G * d * element size exceeds 2^31 - 1 bytes
  *                     or max_seq exceeds 4096 splits of
- *                     gqa_decode_split_keys(B, H, G, max_seq) keys;
+ *                     gqa_decode_split_keys(B, H, G, max_seq) keys, a decode or fp32
+ *                     prefill with B > 65535 (sequences index a grid dimension);
  *       GQA_EWORKSPACE workspace smaller than gqa_workspace_bytes() or NULL when needed;
  *       GQA_EHIP      a HIP launch error.
  *     A batch with B == 0 or T == 0 is valid and enqueues nothing.  Device faults show up

@@ -203,6 +203,7 @@ def test_prefill_mask_checks():
     (dict(q_norm_w=A + 4), _lib.GQA_EINVAL), (dict(cu_seqlens=A + 1), _lib.GQA_EINVAL),
     (dict(workspace=None), _lib.GQA_EWORKSPACE), (dict(workspace_bytes=100), _lib.GQA_EWORKSPACE),
     (dict(B=0), _lib.GQA_OK), (dict(T=0), _lib.GQA_OK), (dict(B=0, q=None), _lib.GQA_OK),
+    (dict(B=65536, T=1, dtype=_lib.GQA_F32), _lib.GQA_ENOTSUP),  # fp32 grid: B on dimension z
 ])
 def test_prefill_rejects_before_launch(kw, code):
     assert _prefill(**kw) == code
@@ -218,6 +219,7 @@ def test_prefill_rejects_before_launch(kw, code):
     (dict(k_new=MIS, v_new=A), _lib.GQA_EINVAL), (dict(positions=A + 1), _lib.GQA_EINVAL),
     (dict(workspace_bytes=10), _lib.GQA_EWORKSPACE),
     (dict(B=0), _lib.GQA_OK), (dict(B=-2), _lib.GQA_EINVAL),
+    (dict(B=65536), _lib.GQA_ENOTSUP),  # sequences index a grid dimension of <= 65535
 ])
 def test_decode_rejects_before_launch(kw, code):
     assert _decode(**kw) == code
