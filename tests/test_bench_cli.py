@@ -1,5 +1,6 @@
-"""Host-side parts of bench.py (CPU): the one-GPU refusal, and the algorithmic work it counts
-for the mask variants, checked against the oracle's own visibility mask."""
+"""Host-side parts of the measurement (CPU): bench.py's one-GPU refusal, and the algorithmic
+work behind every reported rate (FLOPs of plain, masked and cached prefill, bytes of decode),
+counted against the oracle's own visibility mask or the cache rows one by one."""
 import os
 import subprocess
 import sys
@@ -34,3 +35,27 @@ def test_visible_pairs_equals_the_oracle_mask(lengths, window, density):
     for T in lengths:
         want += int(O.visible_keys(T, T, True, window, layout, 64).sum())
     assert bench.visible_pairs(np.array(lengths), window, layout) == want
+
+
+def test_prefill_flops_count_the_oracle_mask():
+    for causal in (True, False):
+        case = W.make_prefill("c", 3, lengths=np.array([1, 70, 5]), H=6, G=3, d=64, causal=causal)
+        pairs = sum(int(O.visible_keys(int(T), int(T), causal).sum()) for T in case.lengths)
+        assert case.flops == 4.0 * 64 * 6 * pairs
+
+
+def test_cached_prefill_flops_count_the_oracle_mask():
+    for causal in (True, False):
+        case = W.make_cached_prefill("c", 5, [3, 9], [0, 17], 64, H=4, G=2, d=64, causal=causal)
+        pairs = sum(int(O.visible_keys(int(T), int(T + P), causal).sum())
+                    for T, P in zip(case.new.lengths, case.cache_lens))
+        assert case.flops == 4.0 * 64 * 4 * pairs
+
+
+def test_decode_bytes_count_every_visible_row():
+    case = W.make_decode("d", 2, B=5, max_seq=300, H=8, G=2, d=64, seq_lens=[0, 1, 77, 300, 5])
+    rows = sum(int(L) for L in case.seq_lens)  # one K and one V row of every group per key
+    assert case.kv_bytes == rows * 2 * 64 * 2 * 2 + 2 * 5 * 8 * 64 * 2
+    steps = W.make_decode_steps("s", 4, [0, 10], 3, 16, H=4, G=2, d=64)
+    rows = sum(int(P) + s + 1 for P in steps.cache_lens for s in range(3))
+    assert steps.kv_bytes == rows * 2 * 64 * 2 * 2 + 2 * 3 * 2 * 4 * 64 * 2
