@@ -32,7 +32,8 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _dev(t, name, dtype=None):
+def _dev(t, name, dtype=None, shape=None):
+    """Device, contiguity, dtype and (when given) shape checks of a caller's tensor."""
     if t is None:
         return None
     if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
@@ -41,25 +42,66 @@ def _dev(t, name, dtype=None):
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    _shape(t, name, shape)
     return t
 
 
-def _params(dtype, q_norm_w, k_norm_w, eps, theta, scale, stream, device, rope_inv_freq=None):
+def _shape(t, name, shape):
+    """Raise unless tensor t (None passes) has exactly ``shape`` (a tuple, or an int for the
+    element count of a 1-D-like array). The library reads and writes whole rows from these
+    sizes, so a wrong shape would become an out-of-bounds device access."""
+    if t is None or shape is None:
+        return
+    if isinstance(shape, int):
+        if t.numel() != shape:
+            raise ValueError(f"{name} must hold {shape} elements, got {t.numel()}")
+    elif tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _rope_table(rope_inv_freq, d):
+    """The caller's RoPE frequency table as a contiguous host float64 array of d/2 entries
+    (the library reads exactly d/2 doubles from it)."""
+    import numpy as np
+    w = np.ascontiguousarray(np.asarray(rope_inv_freq, dtype=np.float64))
+    if w.ndim != 1 or w.shape[0] != d // 2:
+        raise ValueError(f"rope_inv_freq must hold d/2 = {d // 2} frequencies, got shape {w.shape}")
+    return w
+
+
+def _block_mask_check(block_mask, n_keys):
+    """A block mask needs ceil(n_keys / 64) rows of at least ceil(ceil(n_keys / 64) / 32)
+    words (the library reads the rows of every query block of the keys it covers)."""
+    nb = -(-int(n_keys) // 64)
+    if block_mask.dim() != 2:
+        raise ValueError("block_mask must be [rows, words] int32 bit rows")
+    if block_mask.shape[0] < nb or block_mask.shape[1] * 32 < nb:
+        raise ValueError(f"block_mask must have at least {nb} rows of {-(-nb // 32)} words, "
+                         f"got {tuple(block_mask.shape)}")
+
+
+def _params(dtype, d, q_norm_w, k_norm_w, eps, theta, scale, stream, rope_inv_freq=None):
     p = _lib.default_params()
     if rope_inv_freq is not None:
-        import numpy as np
-        w = np.ascontiguousarray(np.asarray(rope_inv_freq, dtype=np.float64).ravel())
+        w = _rope_table(rope_inv_freq, d)
         p._freqs = w  # kept alive with the struct: the library reads it during the call
         p.rope_inv_freq = w.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
     p.dtype = _DTYPES[dtype]
-    p.q_norm_w = _ptr(_dev(q_norm_w, "q_norm_w", dtype))
-    p.k_norm_w = _ptr(_dev(k_norm_w, "k_norm_w", dtype))
+    p.q_norm_w = _ptr(_dev(q_norm_w, "q_norm_w", dtype, (d,)))
+    p.k_norm_w = _ptr(_dev(k_norm_w, "k_norm_w", dtype, (d,)))
     p.eps = float(eps)
     p.rope_theta = float(theta)
     p.scale = float(scale)
-    s = stream if stream is not None else torch.cuda.current_stream(device)
-    p.stream = ctypes.c_void_p(s.cuda_stream)
+    p.stream = ctypes.c_void_p(stream.cuda_stream)
     return p
+
+
+def _stream(stream, device):
+    """The launch stream: the caller's, or torch's current stream on the device. Everything
+    the binding allocates for a call is allocated on this stream (inside
+    ``torch.cuda.stream``), so torch's caching allocator hands that memory out again only
+    behind the call's kernels."""
+    return stream if stream is not None else torch.cuda.current_stream(device)
 
 
 def workspace_bytes(op: str, B: int, T_or_max_seq: int, H: int, G: int, d: int,
@@ -85,36 +127,48 @@ def _prof(p, prof):
     p.prof_stop = ctypes.c_void_p(stop.cuda_event)
 
 
-def _workspace(ws, nbytes, device):
+def _workspace(ws, nbytes, device, stream):
+    """The caller's workspace (checked), or a new one allocated on the launch stream."""
     if ws is None:
-        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(stream):
+            return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
     _dev(ws, "workspace")
     if ws.numel() * ws.element_size() < nbytes:
         raise ValueError(f"workspace needs {nbytes} bytes")
     return ws
 
 
+def _out_like(out, ref, name, stream):
+    """The caller's output tensor (checked against ref's dtype and shape), or a new one like
+    ref allocated on the launch stream."""
+    if out is None:
+        with torch.cuda.stream(stream):
+            return torch.empty_like(ref)
+    return _dev(out, name, ref.dtype, tuple(ref.shape))
+
+
 def rope_freq_table(d, theta=1e6, kind="base", alpha=1.0, train_len=None, infer_len=None,
                     scale=1.0):
-    """The d/2 RoPE frequencies for ``rope_inv_freq`` (host, float64):
+    """The d/2 RoPE frequencies for ``rope_inv_freq`` (host, float64), computed by the
+    library's gqa_rope_freq_table:
     base   omega_j = theta^(-2j/d);
     linear position interpolation by the extension factor alpha: omega_j / alpha;
     yarn   the architecture article's 3.4.2 formula: past train_len, omega_j times
            1 - s 2j/d with s = scale * log2(infer_len / train_len);
     ntk    NTK-aware scaling as a change of base, theta * alpha^(d / (d - 2))."""
     import numpy as np
-    j = np.arange(d // 2, dtype=np.float64)
-    if kind == "ntk":
-        theta = float(theta) * float(alpha) ** (d / (d - 2.0))
-    w = float(theta) ** (-2.0 * j / d)
-    if kind == "linear":
-        w = w / float(alpha)
-    elif kind == "yarn":
-        if infer_len > train_len:
-            w = w * (1.0 - float(scale) * np.log2(infer_len / train_len) * 2.0 * j / d)
-    elif kind not in ("base", "ntk"):
+    kinds = {"base": _lib.GQA_ROPE_BASE, "linear": _lib.GQA_ROPE_LINEAR,
+             "yarn": _lib.GQA_ROPE_YARN, "ntk": _lib.GQA_ROPE_NTK}
+    if kind not in kinds:
         raise ValueError(f"unknown RoPE scaling {kind!r}")
-    return w
+    out = np.empty(int(d) // 2, dtype=np.float64)
+    rc = _lib.load().gqa_rope_freq_table(
+        kinds[kind], int(d), float(theta), float(alpha),
+        float(train_len if train_len is not None else 0.0),
+        float(infer_len if infer_len is not None else 0.0), float(scale),
+        out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+    _lib.check(rc, "gqa_rope_freq_table")
+    return out
 
 
 def pack_block_mask(mask):
@@ -132,12 +186,11 @@ def pack_block_mask(mask):
     return packed.astype(np.uint32).view(np.int32)
 
 
-def _masks(p, window, block_mask):
+def _masks(p, window, block_mask, n_keys):
     p.window = int(window)
     if block_mask is not None:
         _dev(block_mask, "block_mask", torch.int32)
-        if block_mask.dim() != 2:
-            raise ValueError("block_mask must be [rows, words] int32 bit rows")
+        _block_mask_check(block_mask, n_keys)
         p.block_mask = _ptr(block_mask)
         p.block_mask_words = block_mask.shape[1]
 
@@ -153,41 +206,40 @@ def prefill(q, k, v, positions=None, *, causal=True, q_norm_w=None, k_norm_w=Non
     (start, stop) torch.cuda.Event pair recorded around the attention kernel alone.
     window: keep only the `window` most recent keys (causal only); block_mask: device int32
     bit rows over 64-key blocks (``pack_block_mask``). rope_inv_freq: optional d/2 RoPE
-    frequencies (``rope_freq_table``) in place of theta. Returns out like q."""
+    frequencies (``rope_freq_table``) in place of theta. stream: launch stream (default:
+    torch's current stream). Returns out like q."""
     _dev(q, "q")
     dtype = q.dtype
-    _dev(k, "k", dtype)
-    _dev(v, "v", dtype)
     if cu_seqlens is None:
         if q.dim() != 4:
             raise ValueError("dense prefill takes q [B, T, H, d]")
         B, T, H, d = q.shape
-        G = k.shape[2]
-        if k.shape != (B, T, G, d) or v.shape != k.shape:
-            raise ValueError("k and v must be [B, T, G, d]")
+        G = k.shape[2] if isinstance(k, torch.Tensor) and k.dim() == 4 else -1
+        kshape = (B, T, G, d)
     else:
         _dev(cu_seqlens, "cu_seqlens", torch.int32)
         if q.dim() != 3 or max_seqlen is None:
             raise ValueError("packed prefill takes q [N, H, d] and max_seqlen")
         N, H, d = q.shape
-        G = k.shape[1]
+        G = k.shape[1] if isinstance(k, torch.Tensor) and k.dim() == 3 else -1
         B = cu_seqlens.numel() - 1
         T = int(max_seqlen)
-        if k.shape != (N, G, d) or v.shape != k.shape:
-            raise ValueError("k and v must be [N, G, d]")
-    _dev(positions, "positions", torch.int32)
-    _dev(k_out, "k_out", dtype)
-    if out is None:
-        out = torch.empty_like(q)
-    _dev(out, "out", dtype)
-    p = _params(dtype, q_norm_w, k_norm_w, eps, theta, scale, stream, q.device, rope_inv_freq)
+        kshape = (N, G, d)
+    _dev(k, "k", dtype, kshape)
+    _dev(v, "v", dtype, kshape)
+    n_tok = q.numel() // (H * d) if H * d else 0
+    _dev(positions, "positions", torch.int32, n_tok)
+    _dev(k_out, "k_out", dtype, n_tok * G * d)
+    s = _stream(stream, q.device)
+    out = _out_like(out, q, "out", s)
+    p = _params(dtype, d, q_norm_w, k_norm_w, eps, theta, scale, s, rope_inv_freq)
     nbytes = workspace_bytes("prefill", B, T, H, G, d, dtype)
-    ws = _workspace(workspace, nbytes, q.device)
+    ws = _workspace(workspace, nbytes, q.device, s)
     p.workspace = _ptr(ws)
     p.workspace_bytes = ws.numel() * ws.element_size()
     p.cu_seqlens = _ptr(cu_seqlens)
     p.k_out = _ptr(k_out)
-    _masks(p, window, block_mask)
+    _masks(p, window, block_mask, T)
     _prof(p, prof)
     rc = _lib.load().gqa_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(positions), _ptr(out), B, T,
                                  H, G, d, 1 if causal else 0, ctypes.byref(p))
@@ -208,20 +260,16 @@ def prefill_cached(q, k, v, k_cache, v_cache, cache_lens, positions=None, *, cau
     like q."""
     _dev(q, "q")
     dtype = q.dtype
-    _dev(k, "k", dtype)
-    _dev(v, "v", dtype)
     _dev(k_cache, "k_cache", dtype)
-    _dev(v_cache, "v_cache", dtype)
-    _dev(cache_lens, "cache_lens", torch.int32)
-    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+    if k_cache.dim() != 4:
         raise ValueError("caches must be [B, max_seq, G, d]")
+    _dev(v_cache, "v_cache", dtype, tuple(k_cache.shape))
     Bc, S, G, d = k_cache.shape
     if cu_seqlens is None:
         if q.dim() != 4:
             raise ValueError("dense cached prefill takes q [B, T, H, d]")
         B, T, H, d_q = q.shape
-        if k.shape != (B, T, G, d) or v.shape != k.shape:
-            raise ValueError("k and v must be [B, T, G, d]")
+        kshape = (B, T, G, d)
     else:
         _dev(cu_seqlens, "cu_seqlens", torch.int32)
         if q.dim() != 3 or max_seqlen is None:
@@ -229,23 +277,43 @@ def prefill_cached(q, k, v, k_cache, v_cache, cache_lens, positions=None, *, cau
         N, H, d_q = q.shape
         B = cu_seqlens.numel() - 1
         T = int(max_seqlen)
-        if k.shape != (N, G, d) or v.shape != k.shape:
-            raise ValueError("k and v must be [N, G, d]")
+        kshape = (N, G, d)
+    _dev(k, "k", dtype, kshape)
+    _dev(v, "v", dtype, kshape)
+    _dev(cache_lens, "cache_lens", torch.int32)
     if d_q != d or Bc != B or cache_lens.numel() != B:
         raise ValueError("q, caches and cache_lens disagree on B or d")
-    _dev(positions, "positions", torch.int32)
-    if out is None:
-        out = torch.empty_like(q)
-    _dev(out, "out", dtype)
-    p = _params(dtype, q_norm_w, k_norm_w, eps, theta, scale, stream, q.device, rope_inv_freq)
+    _dev(positions, "positions", torch.int32, q.numel() // (H * d) if H * d else 0)
+    s = _stream(stream, q.device)
+    out = _out_like(out, q, "out", s)
+    p = _params(dtype, d, q_norm_w, k_norm_w, eps, theta, scale, s, rope_inv_freq)
     p.cu_seqlens = _ptr(cu_seqlens)
-    _masks(p, window, block_mask)
+    _masks(p, window, block_mask, S)
     _prof(p, prof)
     rc = _lib.load().gqa_prefill_cached(_ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache),
                                         _ptr(cache_lens), _ptr(positions), _ptr(out), B, T, H,
                                         G, d, S, 1 if causal else 0, ctypes.byref(p))
     _lib.check(rc, "gqa_prefill_cached")
     return out
+
+
+def _decode_shapes(q, k_cache, v_cache, seq_lens, k_new, v_new, positions):
+    """Shape checks shared by decode and DecodeGraph; returns (B, H, G, d, max_seq)."""
+    _dev(q, "q")
+    dtype = q.dtype
+    if q.dim() != 3:
+        raise ValueError("decode takes q [B, H, d]")
+    B, H, d = q.shape
+    _dev(k_cache, "k_cache", dtype)
+    if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError("caches must be [B, max_seq, G, d]")
+    _, S, G, _ = k_cache.shape
+    _dev(v_cache, "v_cache", dtype, tuple(k_cache.shape))
+    _dev(seq_lens, "seq_lens", torch.int32, B)
+    _dev(k_new, "k_new", dtype, (B, G, d))
+    _dev(v_new, "v_new", dtype, (B, G, d))
+    _dev(positions, "positions", torch.int32, B)
+    return B, H, G, d, S
 
 
 def decode(q, k_cache, v_cache, seq_lens, *, k_new=None, v_new=None, positions=None,
@@ -256,24 +324,13 @@ def decode(q, k_cache, v_cache, seq_lens, *, k_new=None, v_new=None, positions=N
     normalised/rotated (K) and written at slot seq_lens[b]-1 first. prof: optional
     (start, stop) torch.cuda.Event pair recorded around the split-KV pass alone.
     Returns out [B, H, d]."""
-    _dev(q, "q")
+    B, H, G, d, S = _decode_shapes(q, k_cache, v_cache, seq_lens, k_new, v_new, positions)
     dtype = q.dtype
-    _dev(k_cache, "k_cache", dtype)
-    _dev(v_cache, "v_cache", dtype)
-    _dev(seq_lens, "seq_lens", torch.int32)
-    _dev(k_new, "k_new", dtype)
-    _dev(v_new, "v_new", dtype)
-    _dev(positions, "positions", torch.int32)
-    B, H, d = q.shape
-    _, S, G, d2 = k_cache.shape
-    if d2 != d or v_cache.shape != k_cache.shape or k_cache.shape[0] != B:
-        raise ValueError("caches must be [B, max_seq, G, d]")
-    if out is None:
-        out = torch.empty_like(q)
-    _dev(out, "out", dtype)
-    p = _params(dtype, q_norm_w, k_norm_w, eps, theta, scale, stream, q.device, rope_inv_freq)
+    s = _stream(stream, q.device)
+    out = _out_like(out, q, "out", s)
+    p = _params(dtype, d, q_norm_w, k_norm_w, eps, theta, scale, s, rope_inv_freq)
     nbytes = workspace_bytes("decode", B, S, H, G, d, dtype)
-    ws = _workspace(workspace, nbytes, q.device)
+    ws = _workspace(workspace, nbytes, q.device, s)
     p.workspace = _ptr(ws)
     p.workspace_bytes = ws.numel() * ws.element_size()
     p.k_new = _ptr(k_new)
@@ -301,24 +358,15 @@ class DecodeGraph:
                  q_norm_w=None, k_norm_w=None, eps=1e-6, theta=1e6, scale=0.0, out=None,
                  workspace=None, rope_inv_freq=None):
         self._h = None
-        _dev(q, "q")
-        dtype = q.dtype
-        for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (k_new, "k_new"),
-                     (v_new, "v_new")):
+        for t, n in ((k_new, "k_new"), (v_new, "v_new")):
             if t is None:
                 raise ValueError(f"{n} is required")
-            _dev(t, n, dtype)
-        _dev(seq_lens, "seq_lens", torch.int32)
-        _dev(positions, "positions", torch.int32)
-        B, H, d = q.shape
-        _, S, G, d2 = k_cache.shape
-        if d2 != d or v_cache.shape != k_cache.shape or k_cache.shape[0] != B:
-            raise ValueError("caches must be [B, max_seq, G, d]")
-        if k_new.shape != (B, G, d) or v_new.shape != k_new.shape or seq_lens.numel() != B:
-            raise ValueError("k_new / v_new must be [B, G, d] and seq_lens [B]")
-        out = torch.empty_like(q) if out is None else _dev(out, "out", dtype)
-        p = _params(dtype, q_norm_w, k_norm_w, eps, theta, scale, None, q.device, rope_inv_freq)
-        ws = _workspace(workspace, workspace_bytes("decode", B, S, H, G, d, dtype), q.device)
+        B, H, G, d, S = _decode_shapes(q, k_cache, v_cache, seq_lens, k_new, v_new, positions)
+        dtype = q.dtype
+        s = torch.cuda.current_stream(q.device)
+        out = _out_like(out, q, "out", s)
+        p = _params(dtype, d, q_norm_w, k_norm_w, eps, theta, scale, s, rope_inv_freq)
+        ws = _workspace(workspace, workspace_bytes("decode", B, S, H, G, d, dtype), q.device, s)
         p.workspace = _ptr(ws)
         p.workspace_bytes = ws.numel() * ws.element_size()
         p.k_new = _ptr(k_new)
@@ -336,7 +384,10 @@ class DecodeGraph:
         self._h = h
 
     def launch(self, stream=None):
-        """Enqueue one step on ``stream`` (default: torch's current stream); returns out."""
+        """Enqueue one step on ``stream`` (default: torch's current stream); returns out.
+        The bound tensors (out and the workspace included) belong to the stream the graph
+        was created on: a launch on another stream must be ordered against that one by the
+        caller."""
         if self._h is None:
             raise RuntimeError("the decode graph is closed")
         s = stream if stream is not None else torch.cuda.current_stream(self.device)
@@ -370,14 +421,22 @@ def qk_norm_rope(q, k=None, positions=None, *, q_norm_w=None, k_norm_w=None, eps
     positions: device int32 [N] or None for 0..N-1."""
     _dev(q, "q")
     dtype = q.dtype
+    if q.dim() != 3:
+        raise ValueError("qk_norm_rope takes q [N, H, d]")
     N, H, d = q.shape
-    G = 1 if k is None else k.shape[1]
-    _dev(k, "k", dtype)
-    _dev(positions, "positions", torch.int32)
-    q_out = torch.empty_like(q) if q_out is None else _dev(q_out, "q_out", dtype)
     if k is not None:
-        k_out = torch.empty_like(k) if k_out is None else _dev(k_out, "k_out", dtype)
-    p = _params(dtype, q_norm_w, k_norm_w, eps, theta, 0.0, stream, q.device, rope_inv_freq)
+        _dev(k, "k", dtype)
+        if k.dim() != 3 or k.shape[0] != N or k.shape[2] != d:
+            raise ValueError("k must be [N, G, d]")
+    G = 1 if k is None else k.shape[1]
+    _dev(positions, "positions", torch.int32, N)
+    s = _stream(stream, q.device)
+    q_out = _out_like(q_out, q, "q_out", s)
+    if k is not None:
+        k_out = _out_like(k_out, k, "k_out", s)
+    elif k_out is not None:
+        raise ValueError("k_out needs k")
+    p = _params(dtype, d, q_norm_w, k_norm_w, eps, theta, 0.0, s, rope_inv_freq)
     rc = _lib.load().gqa_qk_norm_rope(_ptr(q), _ptr(k), _ptr(positions), _ptr(q_out),
                                       _ptr(k_out), N, H, G, d, ctypes.byref(p))
     _lib.check(rc, "gqa_qk_norm_rope")

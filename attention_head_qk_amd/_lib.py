@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa.so")
 GQA_OK, GQA_EINVAL, GQA_ENOTSUP, GQA_EWORKSPACE, GQA_EHIP = range(5)
 GQA_F32, GQA_BF16 = 0, 1
 GQA_OP_PREFILL, GQA_OP_DECODE, GQA_OP_QK_NORM_ROPE = 0, 1, 2
+GQA_ROPE_BASE, GQA_ROPE_LINEAR, GQA_ROPE_YARN, GQA_ROPE_NTK = range(4)
 
 # Every function include/gqa.h declares, with its ctypes signature.
 _vp = ctypes.c_void_p
@@ -57,6 +58,8 @@ SIGNATURES = {
     "gqa_qk_norm_rope": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, ctypes.POINTER(GqaParams)]),
     "gqa_workspace_bytes": (ctypes.c_size_t, [_i, _i, _i, _i, _i, _i, _i]),
     "gqa_decode_split_keys": (_i, [_i, _i, _i, _i]),
+    "gqa_rope_freq_table": (_i, [_i, _i, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                 ctypes.c_double, ctypes.c_double, ctypes.POINTER(ctypes.c_double)]),
     "gqa_status_str": (ctypes.c_char_p, [_i]),
 }
 

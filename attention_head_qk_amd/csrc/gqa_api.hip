@@ -252,6 +252,47 @@ const char* gqa_status_str(gqa_status s) {
   return "unknown gqa_status";
 }
 
+gqa_status gqa_rope_freq_table(int kind, int d, double theta, double alpha, double train_len,
+                               double infer_len, double scale, double* out) {
+  if (!out || d < 2 || d > 2 * gqa::kMaxHalfD || d % 2 != 0) return GQA_EINVAL;
+  if (!(theta > 0.0) || !std::isfinite(theta)) return GQA_EINVAL;
+  const int half = d / 2;
+  double base = theta;  // the base whose table is taken before any per-frequency factor
+  switch (kind) {
+    case GQA_ROPE_BASE:
+      break;
+    case GQA_ROPE_LINEAR:
+      if (!(alpha > 0.0) || !std::isfinite(alpha)) return GQA_EINVAL;
+      break;
+    case GQA_ROPE_YARN:
+      if (!(train_len > 0.0) || !(infer_len > 0.0) || !std::isfinite(train_len) ||
+          !std::isfinite(infer_len) || !std::isfinite(scale))
+        return GQA_EINVAL;
+      break;
+    case GQA_ROPE_NTK:
+      if (!(alpha > 0.0) || !std::isfinite(alpha) || d <= 2) return GQA_EINVAL;
+      // theta * alpha^(d / (d - 2)): the exponent makes the last frequency exactly 1/alpha
+      // of its unscaled value
+      base = theta * std::pow(alpha, (double)d / (double)(d - 2));
+      if (!std::isfinite(base) || !(base > 0.0)) return GQA_EINVAL;
+      break;
+    default:
+      return GQA_EINVAL;
+  }
+  // past the training length the YaRN-named rule tilts the table linearly in j
+  const double tilt = (kind == GQA_ROPE_YARN && infer_len > train_len)
+                          ? scale * std::log2(infer_len / train_len)
+                          : 0.0;
+  for (int j = 0; j < half; ++j) {
+    const double frac = 2.0 * j / d;
+    double w = std::pow(base, -frac);
+    if (kind == GQA_ROPE_LINEAR) w /= alpha;
+    if (kind == GQA_ROPE_YARN) w *= 1.0 - tilt * frac;
+    out[j] = w;
+  }
+  return GQA_OK;
+}
+
 int gqa_decode_split_keys(int B, int H, int G, int max_seq) {
   if (B <= 0 || max_seq <= 0 || H <= 0 || G <= 0 || H % G != 0) return 0;
   return decode_split_len(B, H, G, max_seq);

@@ -336,10 +336,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     }
   };
 
-  // ---- buffer descriptors over this (sequence, group)'s K and V rows; rows >= Tkv read as 0
+  // ---- buffer descriptors over this (sequence, group)'s K and V rows. They end at kv_end,
+  // the last key any column of the workgroup sees: rows past it (in the last tile) read as 0,
+  // so nothing past the workgroup's own causal limit is fetched, and a non-finite V value
+  // there never meets the zero weight it would get (0 * inf and 0 * NaN are NaN)
   const int row_bytes = a.G * D * 2;  // bytes between consecutive tokens
   const long base_el = (kvrow0 * a.G + g) * D;
-  const int nrec = (Tkv - 1) * row_bytes + D * 2;
+  const int nrec = (kv_end - 1) * row_bytes + D * 2;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(reinterpret_cast<const bf16_t*>(a.kt) + base_el, nrec);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(reinterpret_cast<const bf16_t*>(a.v) + base_el, nrec);
 

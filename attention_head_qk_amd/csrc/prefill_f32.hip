@@ -91,7 +91,10 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(PrefillArgs a) {
       }
 #pragma unroll
       for (int j = 0; j < SUB; ++j) {
-        const float p = (s[j] == -INFINITY) ? 0.f : expf(s[j] - m);
+        // a key this row does not see adds nothing, not even 0 * v (a non-finite v would
+        // turn that into NaN)
+        if (s[j] == -INFINITY) continue;
+        const float p = expf(s[j] - m);
         l += p;
 #pragma unroll
         for (int e = 0; e < D; ++e) o[e] = fmaf(p, vs[j0 + j][e], o[e]);

@@ -4,37 +4,43 @@ decode split-KV + combine) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload default|...]
 
-A step of the default workload is one pass of the whole path over one batch of synthetic
-input: gqa_prefill on the bf16 prefill T=4096, H=16, G=8, d=128 (causal, gamma ~ U(0.5,1.5),
-theta 1e6), then gqa_decode on 64 sequences x 1 new token with cache lengths U{1024..32768},
-H=32, G=8, d=128 (the new token's K/V appended first). Inputs are resident in HBM before the
-timed region. Prints one JSON line:
+Default workload. A step is one pass of the whole path over one batch of synthetic input,
+inputs resident in HBM before the timed region: gqa_prefill on the bf16 long prefill
+(B=1, T=32768, H=64, G=4, d=128, causal, gamma ~ U(0.5, 1.5), theta 1e6: the largest
+single-GPU configuration), then gqa_decode on 64 sequences x 1 new token with cache lengths
+U{1024..32768}, H=32, G=8, d=128 (the new token's K/V appended first). Prints one JSON line:
 
-* value: prefill TFLOP/s of the whole gqa_prefill call (prologue + attention), algorithmic
-  FLOPs 4*d*H*sum T_b(T_b+1)/2; ``decode`` carries the decode GB/s of the whole gqa_decode
-  call, algorithmic bytes = visible K and V rows + q + out.
-* roofline: the prefill attention kernel alone (HIP events recorded by the library right
-  around its launch, on the launch stream), against the 2.5 PFLOP/s bf16 dense MFMA peak;
-  roofline_decode: the decode split-KV kernel alone against 8 TB/s HBM.
-* --workload chunked: gqa_prefill_cached on 4 sequences, each a 2048-token chunk after a
-  cached prefix of U{2048..14336} tokens (H=32, G=8, d=128); FLOPs count every visible
-  (new query, key) pair, cached keys included.
-* --workload long_window / long_blocks: the T=32768, H=64, G=4 prefill with a 512-key
-  sliding window, or with a 64-key block layout (each query block keeps its previous block
-  and 10% of the earlier ones, seed 9); FLOPs count only the visible (query, key) pairs.
-* --workload decode_loop: a generation loop, 16 sequences from cache lengths U{256..2048};
-  each step advances seq_lens on the device and decodes one token per sequence. value = GB/s
-  of the step replayed as one HIP graph (gqa_decode_graph_*); the eager step (a torch add and
-  gqa_decode) is reported beside it.
-* cpu_baseline: the fp64 CPU oracle timed on the host CPU of the same machine, on a bounded
-  sample of the same prefill workload.
+* value: TFLOP/s of the whole gqa_prefill call (prologue + attention) on the long prefill,
+  algorithmic FLOPs 4*d*H*sum T_b(T_b+1)/2, from the median of per-call HIP-event times.
+* roofline: the prefill attention kernel alone on that workload (HIP events the library
+  records right around its launch, on the launch stream; achieved = FLOPs / mean duration),
+  against the 2.5 PFLOP/s bf16 dense MFMA peak; traffic from the rocprofv3 counter record in
+  profiles/ while the kernel's sources are unchanged, else null.
+* configs: every configuration measured the same way -- the long prefill with G=4 and with
+  G=1 (MQA), the 8-sequence varlen prefill (H=32, G=8), the T=4096 prefill (H=16, G=8), the
+  tiny fp32 prefill and the 64-sequence decode -- each with the whole call and its main
+  kernel (median, min, mean), the rate and the fraction of the roofline.
+* clocks: shader and memory clock samples (sysfs) taken during the timed loops, when the
+  device exposes them.
+* cpu_baseline: the fp64 CPU oracle, unchanged, timed on the host's cores (a pool of
+  processes forked before the GPU is touched, one BLAS thread each) on a bounded sample of
+  every configuration, scaled to the full configuration and labelled so.
+
+Other workloads (--workload): tiny_f32, prefill_4k, varlen, decode, long_g4, long_g1 (one
+configuration each), long_window / long_blocks (the T=32768 G=4 prefill with a 512-key window
+or a 64-key block layout; FLOPs count the visible pairs only), chunked (gqa_prefill_cached: 4
+sequences, each a 2048-token chunk after a cached prefix of U{2048..14336}), decode_loop (a
+generation loop replayed as a HIP graph against the eager step), copy_calibration (a 1 GiB
+device copy for scaling the rocprofv3 byte counters).
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import statistics
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -50,7 +56,7 @@ WINDOW = 512          # sliding-window workload: keys per query
 BLOCK_DENSITY = 0.1   # block-sparse workload: share of earlier 64-key blocks kept
 ROPE_ALPHA = {"linear": 4.0, "ntk": 8.0, "yarn": 1.0}  # --rope-scaling extension factors
 COPY_BYTES = 1 << 30  # bytes read (and written) per step of the copy calibration
-
+MAX_POOL = 16         # CPU workers of the oracle baseline: at most one GPU's share of the host
 
 TRAFFIC_RECORDS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
 
@@ -89,9 +95,9 @@ def log(*a):
 
 def prefill_case(name):
     import workloads as W
-    return {"tiny_f32": W.tiny_f32, "prefill_4k": W.prefill_4k, "default": W.prefill_4k,
-            "varlen": W.prefill_varlen, "long_g4": lambda: W.prefill_long(4),
-            "long_g1": lambda: W.prefill_long(1), "long_window": lambda: W.prefill_long(4),
+    return {"tiny_f32": W.tiny_f32, "prefill_4k": W.prefill_4k, "varlen": W.prefill_varlen,
+            "long_g4": lambda: W.prefill_long(4), "long_g1": lambda: W.prefill_long(1),
+            "long_window": lambda: W.prefill_long(4),
             "long_blocks": lambda: W.prefill_long(4)}[name]()
 
 
@@ -117,6 +123,7 @@ def visible_pairs(lengths, window=0, block_mask=None):
     return total
 
 
+# ----------------------------------------------------------------------------- GPU calls
 class Prefill:
     def __init__(self, case, window=0, block_mask=None, rope_inv_freq=None):
         import torch
@@ -158,10 +165,24 @@ class Prefill:
         c = self.case
         return 4.0 * c.d * c.H * visible_pairs(c.lengths, self.window, self.block_mask)
 
+    @property
+    def kernel(self):
+        import workloads as W
+        return "prefill_bf16_kernel" if self.case.dtype == W.BF16 else "prefill_f32_kernel"
+
+    @property
+    def peak(self):
+        import workloads as W
+        return FP32_PEAK_TFLOPS if self.case.dtype == W.F32 else MFMA_BF16_PEAK_TFLOPS
+
 
 class PrefillCached:
     """gqa_prefill_cached on a chunk workload. Every call appends the same new rows at the
     same cache slots (cache_lens is not advanced), so repeated calls do identical work."""
+
+    kernel = "prefill_bf16_kernel"
+    peak = MFMA_BF16_PEAK_TFLOPS
+    masks = {}
 
     def __init__(self, case):
         import attention_head_qk_amd as gqa
@@ -185,6 +206,8 @@ class PrefillCached:
 
 
 class Decode:
+    kernel = "decode_split_mfma_kernel"
+
     def __init__(self, case):
         import torch
         import attention_head_qk_amd as gqa
@@ -209,43 +232,17 @@ class Decode:
         return self.case.kv_bytes
 
 
-def cpu_baseline(case, budget_s=12.0):
-    """Time the fp64 oracle (as it stands) on whole query heads of the prefill workload,
-    head after head, until about ``budget_s`` seconds of CPU work; report TFLOP/s over the
-    algorithmic FLOPs of the heads done."""
-    import numpy as np
-    from oracle import gqa_oracle as O
-    try:
-        import threadpoolctl
-        cores = max(i["num_threads"] for i in threadpoolctl.threadpool_info()) or 1
-    except Exception:
-        cores = os.cpu_count() or 1
-    q, k, v = case.f64("q"), case.f64("k"), case.f64("v")
-    gq, gk = case.f64("q_norm_w"), case.f64("k_norm_w")
-    t0 = time.perf_counter()
-    qt, kt = O.qk_norm_rope(q, k, case.positions, gq, gk, case.eps, case.theta)
-    h = case.H // case.G
-    heads = 0
-    L = case.lengths.astype(np.float64)
-    per_head = 4.0 * case.d * float(np.sum(L * (L + 1) / 2 if case.causal else L * L))
-    while heads < case.H and (time.perf_counter() - t0) < budget_s:
-        i = heads
-        for b in range(case.B):
-            s, e = int(case.cu_seqlens[b]), int(case.cu_seqlens[b + 1])
-            P = O.attention_weights(qt[s:e, i], kt[s:e, i // h], case.causal)
-            _ = P @ v[s:e, i // h]
-        heads += 1
-    dt = time.perf_counter() - t0
-    return {"value": round(per_head * heads / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"fp64 NumPy oracle on {heads} of {case.H} query heads of {case.name} "
-                      f"(prologue on all tokens + full score matrix per head), {dt:.1f} s"}
+# ----------------------------------------------------------------------------- timing
+def _stats(xs):
+    return {"median": round(statistics.median(xs), 5), "min": round(min(xs), 5),
+            "mean": round(sum(xs) / len(xs), 5)}
 
 
 def timed(fn, steps, warmup):
-    """Warm up, then time ``steps`` calls with events around each whole call, and ``steps``
-    more with events around the main kernel only (recorded by the library on the launch
-    stream), so that neither measurement carries the other's event records."""
+    """Warm up, then ``steps`` calls with events around each whole call, and ``steps`` more
+    with events around the main kernel only (recorded by the library on the launch stream),
+    so that neither measurement carries the other's event records. Returns per-call lists of
+    milliseconds (call, kernel)."""
     import torch
     for _ in range(warmup):
         fn()
@@ -255,21 +252,266 @@ def timed(fn, steps, warmup):
         for x in e:
             x.record()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for e in ev:
         e[0].record()
         fn()
         e[3].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     for e in ev:
         fn(prof=(e[1], e[2]))
     torch.cuda.synchronize()
-    call_ms = sum(e[0].elapsed_time(e[3]) for e in ev) / steps
-    kern_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
-    return wall, call_ms, kern_ms
+    call = [e[0].elapsed_time(e[3]) for e in ev]
+    kern = [e[1].elapsed_time(e[2]) for e in ev]
+    return call, kern
 
 
+class ClockSampler:
+    """Shader and memory clock of the GPU, sampled from sysfs every 20 ms on a thread while
+    the timed loops run (hwmon freq*_input in Hz, else the current pp_dpm level). Reports
+    None for a clock the device does not expose."""
+
+    def __init__(self):
+        import glob
+        self.files = {}
+        for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+            for hw in sorted(glob.glob(dev + "/hwmon/hwmon*")):
+                for lab in glob.glob(hw + "/freq*_label"):
+                    try:
+                        name = open(lab).read().strip().lower()
+                    except OSError:
+                        continue
+                    if name in ("sclk", "mclk") and name not in self.files:
+                        self.files[name] = ("hz", lab.replace("_label", "_input"))
+            for name in ("sclk", "mclk"):
+                f = f"{dev}/pp_dpm_{name}"
+                if name not in self.files and os.path.exists(f):
+                    self.files[name] = ("dpm", f)
+            if self.files:
+                break
+        self.samples = {k: [] for k in self.files}
+        self._stop = threading.Event()
+        self._t = None
+
+    def _read(self, kind, path):
+        try:
+            text = open(path).read()
+        except OSError:
+            return None
+        if kind == "hz":
+            return int(text.strip()) / 1e6
+        for line in text.splitlines():
+            if line.strip().endswith("*"):
+                v = line.split(":")[1].strip().rstrip("*").strip().lower().replace("mhz", "")
+                return float(v)
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            for k, (kind, path) in self.files.items():
+                v = self._read(kind, path)
+                if v is not None:
+                    self.samples[k].append(v)
+            self._stop.wait(0.02)
+
+    def __enter__(self):
+        if self.files:
+            self._t = threading.Thread(target=self._run, daemon=True)
+            self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._t:
+            self._t.join()
+
+    def report(self):
+        out = {"source": "sysfs " + ", ".join(f"{k}:{v[0]}" for k, v in self.files.items())
+               if self.files else None}
+        for k in ("sclk", "mclk"):
+            xs = self.samples.get(k) or []
+            out[k + "_mhz"] = ({"median": round(statistics.median(xs), 1),
+                                "min": round(min(xs), 1), "max": round(max(xs), 1),
+                                "samples": len(xs)} if xs else None)
+        return out
+
+
+def measure(runner, steps, warmup, workload_name):
+    """One configuration's sub-object: the whole call and its main kernel, median / min /
+    mean over ``steps`` calls each, rates and the roofline fraction of the kernel."""
+    call, kern = timed(runner, steps, warmup)
+    cs, ks = _stats(call), _stats(kern)
+    work = runner.work
+    if isinstance(runner, Decode):
+        rate = lambda ms: work / (ms * 1e-3) / 1e9  # noqa: E731
+        unit, peak, bound = "GB/s", HBM_PEAK_GBS, "hbm"
+    else:
+        rate = lambda ms: work / (ms * 1e-3) / 1e12  # noqa: E731
+        unit, peak, bound = "TFLOP/s", runner.peak, "mfma"
+    return {
+        "workload": workload_name, "unit": unit, "work": work,
+        "work_unit": "B" if unit == "GB/s" else "FLOP",
+        "call_ms": cs, "kernel_ms": ks,
+        "call_rate": round(rate(cs["median"]), 3),
+        "kernel_rate": round(rate(ks["mean"]), 3),
+        "kernel_rate_best": round(rate(ks["min"]), 3),
+        "roofline": {"bound": bound, "achieved": round(rate(ks["mean"]), 3), "peak": peak,
+                     "unit": unit, "frac": round(rate(ks["mean"]) / peak, 4),
+                     "frac_median": round(rate(ks["median"]) / peak, 4),
+                     "traffic": measured_traffic(runner.kernel, workload_name),
+                     "kernel": runner.kernel},
+    }
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+# The oracle, as it stands, on a pool of worker processes. The pool is forked before the
+# parent touches the GPU (before torch is imported), so the workers hold no GPU state; the
+# host inputs they need are module globals set before the fork and shared copy-on-write.
+_CASES = {}
+
+
+def _worker_init():
+    try:
+        import threadpoolctl
+        threadpoolctl.threadpool_limits(1)
+    except Exception:
+        pass
+
+
+def _oracle_unit(spec):
+    """Time one unit of oracle work. spec = ("prefill", key, b, head) for one (sequence,
+    query head) of a prefill, ("rows", key, head, rows) for sampled query rows of one head,
+    ("decode", key, b) for one decode sequence. Input preparation (decoding the stored
+    bf16 bits, drawing a decode sequence's cache rows) is not timed."""
+    import numpy as np
+    import workloads as W
+    from oracle import gqa_oracle as O
+    kind, key = spec[0], spec[1]
+    c = _CASES[key]
+    if kind == "decode":
+        b = spec[2]
+        k, v = c.cache_rows(b)
+        args = (c.f64("q")[b], W.to_f64(k, c.dtype), W.to_f64(v, c.dtype), int(c.seq_lens[b]),
+                c.f64("q_norm_w"), c.f64("k_norm_w"), c.eps, c.theta)
+        kw = dict(k_new=c.f64("k_new")[b], v_new=c.f64("v_new")[b])
+        t0 = time.perf_counter()
+        O.decode_one(*args, **kw)
+        return time.perf_counter() - t0, os.getpid()
+    h = c.H // c.G
+    gq, gk = c.f64("q_norm_w"), c.f64("k_norm_w")
+    if kind == "prefill":
+        b, i = spec[2], spec[3]
+        s, e = int(c.cu_seqlens[b]), int(c.cu_seqlens[b + 1])
+        g = i // h
+        q = W.to_f64(c.q[s:e, i:i + 1], c.dtype)
+        k = W.to_f64(c.k[s:e, g:g + 1], c.dtype)
+        v = W.to_f64(c.v[s:e, g:g + 1], c.dtype)
+        t0 = time.perf_counter()
+        O.prefill(q, k, v, c.positions[s:e], np.array([0, e - s]), gq, gk, c.eps, c.theta,
+                  c.causal)
+        return time.perf_counter() - t0, os.getpid()
+    i, rows = spec[2], spec[3]
+    g = i // h
+    q = W.to_f64(c.q[:, i:i + 1], c.dtype)
+    k = W.to_f64(c.k[:, g:g + 1], c.dtype)
+    v = W.to_f64(c.v[:, g:g + 1], c.dtype)
+    t0 = time.perf_counter()
+    O.prefill_rows(q, k, v, c.positions, c.cu_seqlens, rows, gq, gk, c.eps, c.theta, c.causal)
+    return time.perf_counter() - t0, os.getpid()
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _pool_size():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(MAX_POOL, n))
+
+
+def start_oracle_pool(cases):
+    """Fork the worker pool now (before any GPU use) with the host cases in place."""
+    import multiprocessing as mp
+    _CASES.update(cases)
+    return mp.get_context("fork").Pool(_pool_size(), initializer=_worker_init)
+
+
+def _run_units(pool, units):
+    """Run units; the time on C cores is the busiest worker's total (its makespan)."""
+    t0 = time.perf_counter()
+    res = pool.map(_oracle_unit, units, chunksize=1)
+    wall = time.perf_counter() - t0
+    per_pid = {}
+    for dt, pid in res:
+        per_pid[pid] = per_pid.get(pid, 0.0) + dt
+    return max(per_pid.values()), wall
+
+
+def cpu_baseline_all(pool, keys, headline):
+    """Oracle time per configuration on the pool, on a bounded sample of each, scaled to the
+    whole configuration (the oracle materialises every score row, so its cost per prefill
+    row is the same for every row of a sequence, and a decode sequence's cost grows with its
+    length). Returns the cpu_baseline object for the headline configuration with the others
+    under per_config."""
+    import numpy as np
+    per = {}
+    for key in keys:
+        c = _CASES[key]
+        if key.startswith("decode"):
+            # every 4th sequence by length rank; scaled by the cached rows they hold
+            order = np.argsort(c.seq_lens)
+            pick = [int(b) for b in order[::4]]
+            busy, wall = _run_units(pool, [("decode", key, b) for b in pick])
+            scale = float(c.seq_lens.sum()) / float(c.seq_lens[pick].sum())
+            per[key] = {"work": c.kv_bytes, "unit": "GB/s",
+                        "sample": f"{len(pick)} of {c.B} sequences (every 4th by length), "
+                                  f"scaled by cached rows", "scale": round(scale, 3),
+                        "busy_s": busy, "wall_s": wall}
+        elif c.B == 1 and c.N >= 16384:
+            # long prefill: 64 seeded query rows (row 0 and the last among them), all heads
+            rng = np.random.default_rng(12)
+            rows = np.unique(np.concatenate([[0, c.N - 1], rng.integers(0, c.N, 62)]))
+            busy, wall = _run_units(pool, [("rows", key, i, rows) for i in range(c.H)])
+            scale = c.N / len(rows)
+            per[key] = {"work": c.flops, "unit": "TFLOP/s",
+                        "sample": f"{len(rows)} of {c.N} query rows, every head, scaled by "
+                                  f"rows (each row's full score row is materialised)",
+                        "scale": round(scale, 3), "busy_s": busy, "wall_s": wall}
+        else:
+            # (sequence, head) units; the varlen workload takes one head of every group
+            heads = range(c.H) if c.N <= 4096 else range(0, c.H, c.H // c.G)
+            units = [("prefill", key, b, i) for b in range(c.B) for i in heads
+                     if c.cu_seqlens[b + 1] > c.cu_seqlens[b]]
+            scale = c.H / len(heads)
+            per[key] = {"work": c.flops, "unit": "TFLOP/s",
+                        "sample": "every (sequence, head)" if scale == 1 else
+                                  f"{len(heads)} of {c.H} heads (one per group), every "
+                                  f"sequence, scaled by heads",
+                        "scale": round(scale, 3)}
+            per[key]["busy_s"], per[key]["wall_s"] = _run_units(pool, units)
+        e = per[key]
+        e["full_s_extrapolated" if e["scale"] != 1 else "full_s"] = round(e["busy_s"] * e["scale"], 3)
+        full = e["busy_s"] * e["scale"]
+        e["value"] = round(e["work"] / full / (1e9 if e["unit"] == "GB/s" else 1e12), 6)
+        e["busy_s"], e["wall_s"] = round(e["busy_s"], 3), round(e["wall_s"], 3)
+        log(f"bench: oracle {key}: {e['value']} {e['unit']} ({e['sample']})")
+    h = per[headline]
+    return {"value": h["value"], "unit": h["unit"], "cores": _pool_size(), "kind": "oracle",
+            "sample": f"{headline}: {h['sample']}; fp64 NumPy oracle on a pool of "
+                      f"{_pool_size()} processes (one BLAS thread each), time = the busiest "
+                      f"worker's total, x{h['scale']} to the full configuration (extrapolated)",
+            "cpu_model": _cpu_model(), "per_config": per}
+
+
+# ----------------------------------------------------------------------------- other workloads
 def copy_calibration(steps, warmup):
     """A plain device-to-device copy of COPY_BYTES per step (torch's copy kernel). Profiled
     with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, it gives the factor that turns those
@@ -389,6 +631,33 @@ def bench_decode_loop(args, dev_name):
     return 0
 
 
+# ----------------------------------------------------------------------------- main
+METRIC = "GQA prefill TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)"
+
+
+def _config_desc(runner):
+    c = runner.case
+    if isinstance(runner, Decode):
+        return {"B": c.B, "sum_L": int(c.seq_lens.sum()), "max_seq": c.max_seq, "H": c.H,
+                "G": c.G, "d": c.d, "seed": c.seed}
+    d = {"B": c.B, "lengths_sum": c.N, "T_max": c.T_max, "H": c.H, "G": c.G, "d": c.d,
+         "causal": c.causal, "seed": c.seed}
+    if c.B > 1 and len(set(c.lengths.tolist())) > 1:
+        d["lengths"] = c.lengths.tolist()
+    return d
+
+
+def _wname(runner, rope_scaling="none"):
+    name = runner.case.name
+    if getattr(runner, "window", 0):
+        name += f"_window{runner.window}"
+    if getattr(runner, "block_mask", None) is not None:
+        name += "_blocks64"
+    if getattr(runner, "rope", None):
+        name += "_rope_" + rope_scaling
+    return name
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -405,10 +674,25 @@ def main(argv=None):
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
         return 2
+    log(f"bench: workload={args.workload} steps={args.steps} warmup={args.warmup}")
+
+    import workloads as W
+    # host inputs first; the oracle's worker pool is forked before the GPU is touched
+    host = {}
+    if args.workload == "default":
+        host = {"long_g4": W.prefill_long(4), "long_g1": W.prefill_long(1),
+                "varlen": W.prefill_varlen(), "prefill_4k": W.prefill_4k(),
+                "tiny_f32": W.tiny_f32(), "decode": W.decode_64()}
+    elif args.workload in ("tiny_f32", "prefill_4k", "varlen", "long_g4", "long_g1"):
+        host = {args.workload: prefill_case(args.workload)}
+    elif args.workload == "decode":
+        host = {"decode": W.decode_64()}
+    pool = None
+    if host and not args.no_cpu_baseline and args.rope_scaling == "none":
+        pool = start_oracle_pool(host)
+        log(f"bench: oracle pool of {_pool_size()} processes started")
 
     import torch
-    import workloads as W
-    log(f"bench: workload={args.workload} steps={args.steps} warmup={args.warmup}")
     if args.workload == "copy_calibration":
         print(json.dumps(copy_calibration(args.steps, args.warmup)), flush=True)
         return 0
@@ -417,119 +701,91 @@ def main(argv=None):
     if args.workload == "decode_loop":
         return bench_decode_loop(args, dev_name)
 
-    pre = dec = None
+    runners = {}
     if args.workload == "chunked":
-        pre = PrefillCached(W.prefill_chunked())
-        log(f"bench: cached prefill inputs ready ({pre.case.name}, N={pre.case.N})")
-    elif args.rope_scaling != "none" and args.workload != "decode":
-        import attention_head_qk_amd as gqa
-        case = prefill_case(args.workload)
-        table = gqa.rope_freq_table(case.d, case.theta, args.rope_scaling, alpha=ROPE_ALPHA[args.rope_scaling],
-                                    train_len=32768, infer_len=131072)
-        pre = Prefill(case, rope_inv_freq=table)
+        runners["chunked"] = PrefillCached(W.prefill_chunked())
     elif args.workload == "long_window":
-        pre = Prefill(prefill_case(args.workload), window=WINDOW)
+        runners["long_window"] = Prefill(prefill_case("long_window"), window=WINDOW)
     elif args.workload == "long_blocks":
-        case = prefill_case(args.workload)
-        pre = Prefill(case, block_mask=W.make_block_mask(9, -(-case.T_max // 64), BLOCK_DENSITY))
-    elif args.workload != "decode":
-        pre = Prefill(prefill_case(args.workload))
-        log(f"bench: prefill inputs ready ({pre.case.name}, N={pre.case.N})")
-    if args.workload in ("default", "decode"):
-        dec = Decode(W.decode_64())
-        log(f"bench: decode inputs ready ({dec.case.name}, sum L={int(dec.case.seq_lens.sum())})")
+        case = prefill_case("long_blocks")
+        runners["long_blocks"] = Prefill(case, block_mask=W.make_block_mask(
+            9, -(-case.T_max // 64), BLOCK_DENSITY))
+    else:
+        for key, case in host.items():
+            if key == "decode":
+                runners[key] = Decode(case)
+            elif args.rope_scaling != "none":
+                import attention_head_qk_amd as gqa
+                table = gqa.rope_freq_table(case.d, case.theta, args.rope_scaling,
+                                            alpha=ROPE_ALPHA[args.rope_scaling],
+                                            train_len=32768, infer_len=131072)
+                runners[key] = Prefill(case, rope_inv_freq=table)
+            else:
+                runners[key] = Prefill(case)
     torch.cuda.synchronize()
+    log("bench: device inputs ready: " + ", ".join(r.case.name for r in runners.values()))
 
-    def step(prof=None):
-        if pre is not None:
-            pre(prof)
-        if dec is not None:
-            dec()
+    # the step: one pass of the whole path (prefill of the headline configuration, then the
+    # decode) when both are present, else the one configuration
+    head_key = "long_g4" if "long_g4" in runners else next(iter(runners))
+    step_fns = [runners[head_key]] + ([runners["decode"]] if "decode" in runners
+                                      and head_key != "decode" else [])
 
-    # whole-step wall clock (both calls), events per call and per main kernel
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    log(f"bench: {args.steps} steps, {step_ms:.3f} ms/step")
+    def step():
+        for f in step_fns:
+            f()
 
-    res = {}
-    if pre is not None:
-        _, call_ms, kern_ms = timed(pre, args.steps, 1)
-        res["prefill"] = (call_ms, kern_ms)
-        log(f"bench: prefill call {call_ms:.4f} ms, attention kernel {kern_ms:.4f} ms")
-    if dec is not None:
-        _, call_ms, kern_ms = timed(dec, args.steps, 1)
-        res["decode"] = (call_ms, kern_ms)
-        log(f"bench: decode call {call_ms:.4f} ms, split kernel {kern_ms:.4f} ms")
+    sampler = ClockSampler()
+    with sampler:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        log(f"bench: {args.steps} steps, {step_ms:.3f} ms/step")
+        configs = {}
+        for key, r in runners.items():
+            configs[key] = measure(r, args.steps, 1, _wname(r, args.rope_scaling))
+            cfg = configs[key]
+            cfg.update(_config_desc(r))
+            log(f"bench: {key}: call {cfg['call_ms']['median']:.4f} ms, kernel "
+                f"{cfg['kernel_ms']['median']:.4f} ms (median), {cfg['kernel_rate']} "
+                f"{cfg['unit']} = {cfg['roofline']['frac']:.3f} of peak")
 
-    line = {"metric": "GQA prefill TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)",
-            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-            "ms_per_step": round(step_ms, 4), "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "data": "synthetic", "device": dev_name}
-    cfg = {}
-    if pre is not None:
-        c = pre.case
-        call_ms, kern_ms = res["prefill"]
-        tf_call = pre.work / (call_ms * 1e-3) / 1e12
-        tf_kern = pre.work / (kern_ms * 1e-3) / 1e12
-        peak = FP32_PEAK_TFLOPS if c.dtype == W.F32 else MFMA_BF16_PEAK_TFLOPS
-        kname = "prefill_bf16_kernel" if c.dtype == W.BF16 else "prefill_f32_kernel"
-        wname = c.name
-        if getattr(pre, "window", 0):
-            wname += f"_window{pre.window}"
-        if getattr(pre, "block_mask", None) is not None:
-            wname += "_blocks64"
-        if getattr(pre, "rope", None):
-            wname += "_rope_" + args.rope_scaling
-        line.update({"value": round(tf_call, 3), "unit": "TFLOP/s",
-                     "dtype": "f32" if c.dtype == W.F32 else "bf16"})
-        line["roofline"] = {"bound": "mfma", "achieved": round(tf_kern, 3), "peak": peak,
-                            "unit": "TFLOP/s", "frac": round(tf_kern / peak, 4),
-                            "traffic": measured_traffic(kname, wname),
-                            "kernel": kname,
-                            "kernel_ms": round(kern_ms, 5), "flops_per_launch": pre.work}
-        line["prefill"] = {"ms": round(call_ms, 5), "tflops": round(tf_call, 3),
-                           "frac_of_peak": round(tf_call / peak, 4)}
-        cfg["prefill"] = {"name": wname, "B": c.B, "lengths_sum": c.N, "T_max": c.T_max, "H": c.H,
-                          "G": c.G, "d": c.d, "causal": c.causal, "seed": c.seed}
-        if isinstance(pre, PrefillCached):
-            cfg["prefill"].update(cache_lens=c.cache_lens.tolist(), max_seq=c.max_seq)
-        if getattr(pre, "window", 0):
-            cfg["prefill"]["window"] = pre.window
-        if getattr(pre, "rope", None):
-            cfg["prefill"]["rope_scaling"] = args.rope_scaling
-        if getattr(pre, "block_mask", None) is not None:
-            cfg["prefill"]["block_mask"] = {"block": 64, "kept": int(pre.block_mask.sum()),
-                                            "density": BLOCK_DENSITY, "local": 1, "seed": 9}
-    if dec is not None:
-        c = dec.case
-        call_ms, kern_ms = res["decode"]
-        gbs_call = dec.work / (call_ms * 1e-3) / 1e9
-        gbs_kern = dec.work / (kern_ms * 1e-3) / 1e9
-        line["decode"] = {"value": round(gbs_call, 2), "unit": "GB/s", "ms": round(call_ms, 5),
-                          "frac_of_peak": round(gbs_call / HBM_PEAK_GBS, 4),
-                          "bytes": dec.work}
-        line["roofline_decode"] = {"bound": "hbm", "achieved": round(gbs_kern, 2),
-                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                   "frac": round(gbs_kern / HBM_PEAK_GBS, 4),
-                                   "traffic": measured_traffic("decode_split_mfma_kernel", c.name),
-                                   "kernel": "decode_split_mfma_kernel", "kernel_ms": round(kern_ms, 5)}
-        cfg["decode"] = {"name": c.name, "B": c.B, "sum_L": int(c.seq_lens.sum()), "max_seq": c.max_seq,
-                         "H": c.H, "G": c.G, "d": c.d, "seed": c.seed}
-        if pre is None:
-            line.update({"value": round(gbs_call, 2), "unit": "GB/s", "dtype": "bf16",
-                         "roofline": line.pop("roofline_decode")})
-    names = [v["name"] for v in cfg.values()]
-    line["config"] = {"workload": " + ".join(names), **cfg}
-    if (not args.no_cpu_baseline and pre is not None and not isinstance(pre, PrefillCached)
-            and not pre.masks):
+    head = configs[head_key]
+    hr = runners[head_key]
+    dtype = "f32" if head_key == "tiny_f32" else "bf16"
+    line = {"metric": METRIC, "value": head["call_rate"], "unit": head["unit"], "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+            "data": "synthetic", "device": dev_name}
+    roof = dict(head["roofline"])
+    roof["kernel_ms"] = head["kernel_ms"]["mean"]
+    roof["work_per_launch"] = head["work"]
+    line["roofline"] = roof
+    line["config"] = {"workload": head["workload"], "step": " + ".join(
+        configs[k]["workload"] for k in ([head_key] + (["decode"] if len(step_fns) > 1 else []))),
+        **_config_desc(hr)}
+    if getattr(hr, "window", 0):
+        line["config"]["window"] = hr.window
+    if getattr(hr, "block_mask", None) is not None:
+        line["config"]["block_mask"] = {"block": 64, "kept": int(hr.block_mask.sum()),
+                                        "density": BLOCK_DENSITY, "local": 1, "seed": 9}
+    if args.rope_scaling != "none":
+        line["config"]["rope_scaling"] = args.rope_scaling
+    if isinstance(hr, PrefillCached):
+        line["config"].update(cache_lens=hr.case.cache_lens.tolist(), max_seq=hr.case.max_seq)
+    line["configs"] = configs
+    line["clocks"] = sampler.report()
+    if pool is not None:
         log("bench: timing the CPU oracle")
-        line["cpu_baseline"] = cpu_baseline(pre.case)
+        try:
+            line["cpu_baseline"] = cpu_baseline_all(pool, list(host), head_key)
+        finally:
+            pool.terminate()
     elif not args.no_cpu_baseline:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -54,7 +54,17 @@
  *     seq_lens, cu_seqlens) are trusted: out-of-range values are undefined behaviour,
  *     except a sequence of length 0 (no rows; decode writes zeros).  Nothing is printed and
  *     no C++ exception crosses this interface.
- *   - NaN or Inf inputs propagate to the outputs they touch.
+ *   - Non-finite inputs.  A NaN or infinity in q (token t, head i) reaches out[t, i] only
+ *     (after the RMSNorm an infinite element makes its head row NaN).  One in the K row of
+ *     token t, group g reaches exactly the outputs of group g's query heads whose queries
+ *     see key t (a K row already in a cache skips the norm: there an infinity gives scores
+ *     of +-inf, and -inf only drops that key).  One in the V row of token t, group g reaches those outputs too; the fp32
+ *     prefill and decode stop there, while the bf16 prefill may also turn NaN the outputs of
+ *     group g's heads at the other query positions of the same 128-column block (128 / h
+ *     consecutive positions) that do not see key t, because its products multiply whole
+ *     64-key tiles of V by weights that are exactly 0 for the keys a query does not see
+ *     (and 0 * inf = 0 * NaN = NaN).  Cache rows at or past a sequence's length are never
+ *     read.
  */
 #ifndef GQA_H
 #define GQA_H
@@ -223,6 +233,35 @@ gqa_status gqa_decode_graph_destroy(gqa_decode_graph *graph);
 gqa_status gqa_qk_norm_rope(const void *q, const void *k, const int32_t *positions,
                             void *q_out, void *k_out, int N, int H, int G, int d,
                             const gqa_params *p);
+
+/* RoPE frequency tables for gqa_params.rope_inv_freq: writes the d/2 frequencies omega_j,
+ * j = 0 .. d/2 - 1, of one rule into the caller's HOST array out[d/2], in fp64.
+ *   GQA_ROPE_BASE    omega_j = theta^(-2j/d) (ewbang.com "深入剖析Qwen3模型架构", 3.4.1).
+ *   GQA_ROPE_LINEAR  linear position interpolation by the extension factor alpha: every
+ *                    position index divided by alpha, i.e. omega_j / alpha (zizhi168.cn
+ *                    Qwen3 technical-report summary, 4.2).  alpha > 0.
+ *   GQA_ROPE_YARN    the scaling the architecture article prints under the name YaRN (3.4.2):
+ *                    when infer_len > train_len, omega_j * (1 - s * 2j / d) with
+ *                    s = scale * log2(infer_len / train_len); otherwise the base table.  No
+ *                    ramp and no attention temperature (it is not the published YaRN); past
+ *                    infer_len / train_len = 2^(1/scale) the lowest frequencies turn negative,
+ *                    which is what the formula gives.  train_len, infer_len > 0.
+ *   GQA_ROPE_NTK     NTK-aware scaling read as a change of base (summary, 4.2): the base table
+ *                    of theta * alpha^(d / (d - 2)), which keeps omega_0 and divides
+ *                    omega_{d/2-1} by alpha.  alpha > 0, d > 2.
+ * Arguments a rule does not use are ignored.  d must be even, 2 <= d <= 128; theta > 0 and
+ * every used argument finite.  Returns GQA_EINVAL (nothing written) for a NULL out, an
+ * unknown kind or an argument out of range, GQA_OK otherwise.  Pure host arithmetic: no HIP
+ * call, no device needed. */
+typedef enum gqa_rope_kind {
+  GQA_ROPE_BASE = 0,
+  GQA_ROPE_LINEAR = 1,
+  GQA_ROPE_YARN = 2,
+  GQA_ROPE_NTK = 3
+} gqa_rope_kind;
+
+gqa_status gqa_rope_freq_table(int kind, int d, double theta, double alpha, double train_len,
+                               double infer_len, double scale, double *out);
 
 /* Bytes of workspace an entry point needs (0 when none).  op is a gqa_op, T_or_max_seq is
  * T for prefill and max_seq for decode, dtype a gqa_dtype.  Returns 0 for invalid sizes. */

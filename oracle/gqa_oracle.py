@@ -220,10 +220,14 @@ def prefill(q, k, v, positions, cu_seqlens, q_norm_w, k_norm_w, eps, theta, caus
 
 
 def prefill_rows(q, k, v, positions, cu_seqlens, rows, q_norm_w, k_norm_w, eps, theta,
-                 causal=True, scale=None, window=0, block_mask=None, block=64):
+                 causal=True, scale=None, window=0, block_mask=None, block=64,
+                 max_elems=1 << 26):
     """Selected output rows of ``prefill``: rows are packed token indices. Each row is the
-    same definition evaluated for that query token alone (its full score row over the
-    visible keys of its sequence). Returns [len(rows), H, d]."""
+    same definition evaluated for that query token alone: its full score row over the keys
+    of its sequence, masked by ``visible_keys`` at its index, softmax, times V (Qwen3 series
+    1, D1-4, D1-5, D1-2). The rows of one sequence are evaluated together as one matrix per
+    KV head: S = Q~[rows, heads of g] K~_g^T, in batches of rows of at most ``max_elems``
+    scores (rows are independent, so batching changes nothing). Returns [len(rows), H, d]."""
     rows = np.asarray(rows, dtype=np.int64)
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     H, d = q.shape[1], q.shape[2]
@@ -231,22 +235,27 @@ def prefill_rows(q, k, v, positions, cu_seqlens, rows, q_norm_w, k_norm_w, eps, 
     h = H // G
     out = np.empty((len(rows), H, d), dtype=np.float64)
     seq_of = np.searchsorted(cu, rows, side="right") - 1
-    kt_cache = {}
-    for n, (t, b) in enumerate(zip(rows, seq_of)):
+    for b in np.unique(seq_of):
         s, e = int(cu[b]), int(cu[b + 1])
-        if b not in kt_cache:
-            kt_cache = {b: rope(rms_norm(np.asarray(k[s:e], np.float64), k_norm_w, eps),
-                                positions[s:e], theta)}
-        kt = kt_cache[b]
-        qt = rope(rms_norm(np.asarray(q[t:t + 1], np.float64), q_norm_w, eps),
-                  positions[t:t + 1], theta)[0]
-        r = int(t - s)
-        vis = visible_keys(1, e - s, causal, window, block_mask, block, q_index=[r])[0]
-        vb = np.asarray(v[s:e], np.float64)[vis]
-        for i in range(H):
-            g = i // h
-            p = attention_weights(qt[i:i + 1], kt[vis, g, :], False, scale)[0]
-            out[n, i, :] = p @ vb[:, g, :]
+        sel = np.flatnonzero(seq_of == b)
+        kt = rope(rms_norm(np.asarray(k[s:e], np.float64), k_norm_w, eps), positions[s:e],
+                  theta)
+        vb = np.asarray(v[s:e], np.float64)
+        qt = rope(rms_norm(np.asarray(q[rows[sel]], np.float64), q_norm_w, eps),
+                  np.asarray(positions)[rows[sel]], theta)
+        r_in = rows[sel] - s  # index of each row inside its sequence
+        Tk = e - s
+        step = max(1, max_elems // max(1, h * Tk))
+        for c0 in range(0, len(sel), step):
+            c = slice(c0, c0 + step)
+            vis = visible_keys(len(r_in[c]), Tk, causal, window, block_mask, block,
+                               q_index=r_in[c])
+            for g in range(G):
+                Q = qt[c, g * h:(g + 1) * h, :].reshape(-1, d)  # [rows * h, d]
+                S = (Q @ kt[:, g, :].T) * _scale(d, scale)
+                S = np.where(np.repeat(vis, h, axis=0), S, -np.inf)
+                P = softmax_rows(S)
+                out[sel[c], g * h:(g + 1) * h, :] = (P @ vb[:, g, :]).reshape(-1, h, d)
     return out
 
 

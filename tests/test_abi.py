@@ -102,6 +102,90 @@ def test_rope_freq_table_matches_the_oracle_tables():
                            O.rope_inv_freq(d, O.ntk_theta(1e6, 4.0, d)), rtol=1e-12)
 
 
+def test_rope_freq_table_c_function_pinned():
+    # gqa_rope_freq_table called through ctypes directly, against the oracle's own rules, at
+    # several sizes and arguments, including the YaRN-named rule below the training length
+    # (unchanged) and past 2^(1/scale) times it (the lowest frequencies turn negative)
+    import numpy as np
+    from oracle import gqa_oracle as O
+    f = _lib.load().gqa_rope_freq_table
+
+    def table(kind, d, theta=1e6, alpha=1.0, train=0.0, infer=0.0, scale=1.0):
+        out = np.full(d // 2, -7.0)
+        rc = f(kind, d, theta, alpha, train, infer, scale,
+               out.ctypes.data_as(ctypes.POINTER(ctypes.c_double)))
+        return rc, out
+
+    for d in (2, 8, 64, 128):
+        for theta in (1e4, 1e6):
+            rc, w = table(_lib.GQA_ROPE_BASE, d, theta)
+            assert rc == _lib.GQA_OK and np.allclose(w, O.rope_inv_freq(d, theta), rtol=1e-14)
+            for alpha in (0.5, 4.0, 16.0):
+                rc, w = table(_lib.GQA_ROPE_LINEAR, d, theta, alpha)
+                assert rc == _lib.GQA_OK
+                assert np.allclose(w, O.inv_freq_linear(d, theta, alpha), rtol=1e-14)
+                if d > 2:
+                    rc, w = table(_lib.GQA_ROPE_NTK, d, theta, alpha)
+                    assert rc == _lib.GQA_OK
+                    assert np.allclose(w, O.rope_inv_freq(d, O.ntk_theta(theta, alpha, d)),
+                                       rtol=1e-12)
+            for train, infer, scale in ((32768, 131072, 1.0), (4096, 32768, 0.5),
+                                        (8192, 4096, 1.0), (1000, 1000, 2.0), (2048, 65536, 0.1)):
+                rc, w = table(_lib.GQA_ROPE_YARN, d, theta, 1.0, train, infer, scale)
+                assert rc == _lib.GQA_OK
+                want = O.inv_freq_yarn_page(d, theta, train, infer, scale)
+                assert np.allclose(w, want, rtol=1e-12, atol=1e-300), (d, train, infer, scale)
+    # errors: nothing written
+    for args in ((7, 64, 1e6), (_lib.GQA_ROPE_BASE, 63, 1e6), (_lib.GQA_ROPE_BASE, 130, 1e6),
+                 (_lib.GQA_ROPE_BASE, 0, 1e6), (_lib.GQA_ROPE_BASE, 64, 0.0),
+                 (_lib.GQA_ROPE_BASE, 64, float("inf")), (_lib.GQA_ROPE_BASE, 64, -1.0)):
+        rc, w = table(*args)
+        assert rc == _lib.GQA_EINVAL and np.all(w == -7.0), args
+    assert table(_lib.GQA_ROPE_LINEAR, 64, 1e6, 0.0)[0] == _lib.GQA_EINVAL
+    assert table(_lib.GQA_ROPE_NTK, 64, 1e6, -2.0)[0] == _lib.GQA_EINVAL
+    assert table(_lib.GQA_ROPE_NTK, 2, 1e6, 2.0)[0] == _lib.GQA_EINVAL
+    assert table(_lib.GQA_ROPE_YARN, 64, 1e6, 1.0, 0.0, 100.0)[0] == _lib.GQA_EINVAL
+    assert table(_lib.GQA_ROPE_YARN, 64, 1e6, 1.0, 100.0, 400.0, float("nan"))[0] == _lib.GQA_EINVAL
+    assert f(_lib.GQA_ROPE_BASE, 64, 1e6, 1.0, 0.0, 0.0, 1.0, None) == _lib.GQA_EINVAL
+
+
+def test_binding_computes_no_frequencies():
+    # the binding's rope_freq_table marshals only: its source has no power or log of its own
+    import inspect
+    import attention_head_qk_amd as gqa
+    src = inspect.getsource(gqa.rope_freq_table)
+    for token in ("**", "np.power", "np.log", "math.", "np.arange"):
+        assert token not in src, token
+
+
+def test_binding_shape_checks():
+    # the checks that keep a wrong shape from becoming an out-of-bounds device access; they
+    # look at shapes only, so CPU tensors serve
+    import numpy as np
+    import torch
+    import attention_head_qk_amd as gqa
+    t = torch.zeros(4, 3, 8)
+    gqa._shape(t, "t", (4, 3, 8))
+    gqa._shape(t, "t", 96)
+    gqa._shape(None, "t", (1,))
+    for bad in ((4, 3, 7), (3, 4, 8), (4, 24), 95):
+        with pytest.raises(ValueError):
+            gqa._shape(t, "t", bad)
+    assert gqa._rope_table(np.ones(64), 128).shape == (64,)
+    for bad in (np.ones(63), np.ones(65), np.ones((8, 8)), np.ones(32)):
+        with pytest.raises(ValueError):
+            gqa._rope_table(bad, 128)
+    bm = torch.zeros(64, 2, dtype=torch.int32)
+    gqa._block_mask_check(bm, 4096)
+    gqa._block_mask_check(bm, 64 * 64)
+    with pytest.raises(ValueError):
+        gqa._block_mask_check(bm, 64 * 64 + 1)  # one query block too many
+    with pytest.raises(ValueError):
+        gqa._block_mask_check(torch.zeros(130, 4, dtype=torch.int32), 130 * 64)  # 5 words needed
+    with pytest.raises(ValueError):
+        gqa._block_mask_check(torch.zeros(64, dtype=torch.int32), 64)
+
+
 def test_status_strings():
     for code, tag in [(0, "GQA_OK"), (1, "GQA_EINVAL"), (2, "GQA_ENOTSUP"),
                       (3, "GQA_EWORKSPACE"), (4, "GQA_EHIP")]:

@@ -59,3 +59,27 @@ def test_decode_bytes_count_every_visible_row():
     steps = W.make_decode_steps("s", 4, [0, 10], 3, 16, H=4, G=2, d=64)
     rows = sum(int(P) + s + 1 for P in steps.cache_lens for s in range(3))
     assert steps.kv_bytes == rows * 2 * 64 * 2 * 2 + 2 * 3 * 2 * 4 * 64 * 2
+
+
+def test_cpu_baseline_leg_on_small_cases():
+    # the oracle baseline's pool, units and scaling, on small stand-ins of each kind of
+    # configuration (a full prefill, a long single sequence timed on sampled rows, a varlen
+    # batch timed on one head per group, a decode timed on every 4th sequence)
+    cases = {"tiny_f32": W.make_prefill("t", 1, lengths=[100], H=4, G=2, d=64, dtype=W.F32),
+             "long_x": W.make_prefill("l", 2, lengths=[16384], H=2, G=1, d=64),
+             "varlen_x": W.make_prefill("v", 3, lengths=[300, 5000, 700], H=8, G=2, d=64),
+             "decode": W.make_decode("d", 4, B=8, max_seq=600, H=4, G=2, d=64,
+                                     seq_lens=[1, 600, 30, 200, 7, 64, 599, 2])}
+    pool = bench.start_oracle_pool(cases)
+    try:
+        out = bench.cpu_baseline_all(pool, list(cases), "long_x")
+    finally:
+        pool.terminate()
+    per = out["per_config"]
+    assert out["kind"] == "oracle" and out["unit"] == "TFLOP/s" and out["cores"] >= 1
+    assert out["value"] == per["long_x"]["value"] > 0
+    assert per["tiny_f32"]["scale"] == 1 and "full_s" in per["tiny_f32"]
+    assert per["long_x"]["scale"] == 16384 / 64
+    assert per["varlen_x"]["scale"] == 4 and per["decode"]["unit"] == "GB/s"
+    lens = np.sort(cases["decode"].seq_lens)
+    assert abs(per["decode"]["scale"] - lens.sum() / lens[::4].sum()) < 1e-3

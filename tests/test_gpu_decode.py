@@ -12,20 +12,21 @@ from _gpu import (check, device_decode_inputs, i32, oracle_decode_seq, run_decod
 pytestmark = pytest.mark.gpu
 
 
-def test_decode_64_sequences_sampled():
+def test_decode_64_sequences_all():
+    # every sequence of the 64-sequence workload, and every appended K/V row
+    import _oracle_pool as OP
     case = W.decode_64()
     say("decode 64 seqs, cache", case.max_seq, "lens", int(case.seq_lens.min()), int(case.seq_lens.max()))
     dev = device_decode_inputs(case)
     out = to_f64(run_decode(case, dev))
-    order = np.argsort(case.seq_lens)
-    picks = sorted({int(order[0]), int(order[1]), int(order[-1]), int(order[-2]), 0, 17, 40, 63})
-    for b in picks:
-        want, k_slot, v_slot = oracle_decode_seq(case, b)
-        check(out[b], want, W.BF16, f"seq {b} L={case.seq_lens[b]}")
+    want, k_slots, v_slots = OP.decode_all(case)
+    stats = check(out, want, W.BF16, case.name)
+    say(case.name, stats)
+    for b in range(case.B):
         L = int(case.seq_lens[b])
         got_k = to_f64(dev["k_cache"][b, L - 1])
-        assert np.all(np.abs(got_k - k_slot) <= 2.0 ** -8 * np.abs(k_slot) + 1e-6)
-        assert np.array_equal(to_f64(dev["v_cache"][b, L - 1]), v_slot)
+        assert np.all(np.abs(got_k - k_slots[b]) <= 2.0 ** -8 * np.abs(k_slots[b]) + 1e-6), b
+        assert np.array_equal(to_f64(dev["v_cache"][b, L - 1]), v_slots[b]), b
 
 
 def edge_lens(S):

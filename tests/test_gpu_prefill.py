@@ -28,21 +28,29 @@ def test_bf16_4k_full():
     say(case.name, stats)
 
 
-def test_varlen_packed_sampled_rows():
+def test_varlen_packed_full():
+    # every element of the 8-sequence varlen workload (the oracle per (sequence, head) on a
+    # thread pool)
+    import _oracle_pool as OP
     case = W.prefill_varlen()
-    say("prefill varlen packed", case.lengths.tolist())
+    say("prefill varlen packed, full tensor", case.lengths.tolist())
     got = to_f64(run_prefill(case))
-    rows = sample_rows(case, 48, seed=3)
-    check(got[rows], oracle_prefill_rows(case, rows), W.BF16, case.name)
+    stats = check(got, OP.prefill_full(case), W.BF16, case.name)
+    say(case.name, stats)
 
 
 @pytest.mark.parametrize("G", [4, 1])
 def test_long_32k_sampled_rows(G):
+    # at least 512 query rows with every head: rows 0, 1, the last rows, both sides of key-tile
+    # and column-block boundaries, the rest seeded uniform
+    import _oracle_pool as OP
     case = W.prefill_long(G)
     say(f"prefill long T=32768 H=64 G={G}")
     got = to_f64(run_prefill(case))
-    rows = sample_rows(case, 24, seed=G)
-    check(got[rows], oracle_prefill_rows(case, rows), W.BF16, case.name)
+    rows = OP.sample_rows(case, 512, seed=G)
+    assert len(rows) >= 512 and rows[0] == 0 and rows[-1] == case.N - 1
+    stats = check(got[rows], oracle_prefill_rows(case, rows), W.BF16, case.name)
+    say(case.name, len(rows), "rows", stats)
 
 
 SHAPES = [

@@ -16,10 +16,19 @@ pytestmark = pytest.mark.gpu
 
 
 def _tables(d):
+    """The library's tables (gqa_rope_freq_table): what the GPU side is given."""
     import attention_head_qk_amd as gqa
     return {"linear": gqa.rope_freq_table(d, 1e6, "linear", alpha=4.0),
             "yarn": gqa.rope_freq_table(d, 1e6, "yarn", train_len=32768, infer_len=131072),
             "ntk": gqa.rope_freq_table(d, 1e6, "ntk", alpha=8.0)}
+
+
+def _oracle_tables(d):
+    """The same rules from the oracle's own functions: what the oracle side is given."""
+    from oracle import gqa_oracle as O
+    return {"linear": O.inv_freq_linear(d, 1e6, 4.0),
+            "yarn": O.inv_freq_yarn_page(d, 1e6, 32768, 131072),
+            "ntk": O.rope_inv_freq(d, O.ntk_theta(1e6, 8.0, d))}
 
 
 def _with_theta(case, table):
@@ -39,10 +48,10 @@ def test_prefill_with_table(kind, dtype, d):
     pos = np.concatenate([np.arange(70) * 97 + 5000, np.arange(150) * 211]).astype(np.int32)
     case = W.make_prefill(f"rope_{kind}", 200 + d, lengths=lengths, H=16, G=4, d=d, dtype=dtype,
                           positions=pos)
-    table = _tables(d)[kind]
     say("prefill rope table", kind, dtype, d)
-    got = to_f64(run_prefill(case, rope_inv_freq=table))
-    check(got, oracle_prefill(_with_theta(case, table)), dtype, f"{kind} {dtype} d={d}")
+    got = to_f64(run_prefill(case, rope_inv_freq=_tables(d)[kind]))
+    check(got, oracle_prefill(_with_theta(case, _oracle_tables(d)[kind])), dtype,
+          f"{kind} {dtype} d={d}")
 
 
 def test_base_table_is_the_theta_path():
@@ -58,13 +67,14 @@ def test_base_table_is_the_theta_path():
 def test_decode_and_cached_prefill_with_table():
     from oracle import gqa_oracle as O
     table = _tables(128)["yarn"]
+    otable = _oracle_tables(128)["yarn"]
     # decode
     dcase = W.make_decode("rope_dec", 220, B=4, max_seq=3000, H=32, G=8, d=128,
                           seq_lens=[1, 700, 2999, 64])
     dev = device_decode_inputs(dcase)
     say("decode rope table")
     out = to_f64(run_decode(dcase, dev, rope_inv_freq=table))
-    dcase_t = _with_theta(dcase, table)
+    dcase_t = _with_theta(dcase, otable)
     for b in range(dcase.B):
         want, k_slot, _ = oracle_decode_seq(dcase_t, b)
         check(out[b], want, W.BF16, f"decode b={b}")
@@ -77,7 +87,7 @@ def test_decode_and_cached_prefill_with_table():
     say("cached prefill rope table")
     got = to_f64(run_prefill_cached(ccase, cdev, rope_inv_freq=table))
     from _gpu import oracle_prefill_cached_seq
-    ct = _with_theta(ccase, table)
+    ct = _with_theta(ccase, otable)
     for b in range(ccase.B):
         s, e = int(ccase.cu_seqlens[b]), int(ccase.cu_seqlens[b + 1])
         want, kc, _ = oracle_prefill_cached_seq(ct, b)
@@ -93,6 +103,7 @@ def test_prologue_with_table(dtype):
     from oracle import gqa_oracle as O
     from _gpu import to_dev, i32
     table = _tables(128)["linear"]
+    otable = _oracle_tables(128)["linear"]
     case = W.make_prefill("rope_pro", 230, lengths=[257], H=8, G=2, d=128, dtype=dtype,
                           positions=(np.arange(257) * 31).astype(np.int32))
     say("prologue rope table", dtype)
@@ -100,7 +111,7 @@ def test_prologue_with_table(dtype):
                               q_norm_w=to_dev(case.q_norm_w, dtype),
                               k_norm_w=to_dev(case.k_norm_w, dtype), rope_inv_freq=table)
     qt, kt = O.qk_norm_rope(case.f64("q"), case.f64("k"), case.positions, case.f64("q_norm_w"),
-                            case.f64("k_norm_w"), case.eps, table)
+                            case.f64("k_norm_w"), case.eps, otable)
     tol = 2.0 ** -8 if dtype == W.BF16 else 1e-6
     for got, want in ((to_f64(qo), qt), (to_f64(ko), kt)):
         assert np.all(np.abs(got - want) <= tol * np.abs(want) + 1e-6)

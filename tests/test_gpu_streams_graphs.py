@@ -106,3 +106,44 @@ def test_two_streams_do_not_interfere():
     torch.cuda.synchronize()
     for o, e in zip(outs, eager):
         assert torch.equal(o, e)
+
+
+def test_stream_argument_allocates_on_that_stream():
+    # prefill(..., stream=s) and decode(..., stream=s) with no workspace or out: the binding
+    # allocates both on s, so memory the current stream grabs (and writes) right after the
+    # call can never be the workspace or the output still in use by s's kernels
+    import attention_head_qk_amd as gqa
+    case = W.make_prefill("stream_arg", 420, lengths=[3000], H=16, G=8)
+    dev = device_prefill_inputs(case)
+    shp = lambda t, G: t.view(1, case.N, G, case.d)  # noqa: E731
+    eager = gqa.prefill(shp(dev["q"], case.H), shp(dev["k"], case.G), shp(dev["v"], case.G),
+                        None, q_norm_w=dev["q_norm_w"], k_norm_w=dev["k_norm_w"], eps=case.eps,
+                        theta=case.theta).clone()
+    dcase = W.make_decode("stream_arg_dec", 421, B=4, max_seq=4096, H=32, G=8, d=128,
+                          seq_lens=[4096, 17, 2000, 1025])
+    ddev = device_decode_inputs(dcase)
+    dkw = dict(q_norm_w=ddev["q_norm_w"], k_norm_w=ddev["k_norm_w"], eps=dcase.eps,
+               theta=dcase.theta)
+    d_eager = gqa.decode(ddev["q"], ddev["k_cache"], ddev["v_cache"], ddev["seq_lens"],
+                         **dkw).clone()
+    torch.cuda.synchronize()
+    say("prefill and decode with stream= and binding-allocated buffers")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        # keep s busy first, so its prefill is still running when the current stream moves on
+        with torch.cuda.stream(s):
+            torch.cuda._sleep(2_000_000)
+        out = gqa.prefill(shp(dev["q"], case.H), shp(dev["k"], case.G), shp(dev["v"], case.G),
+                          None, q_norm_w=dev["q_norm_w"], k_norm_w=dev["k_norm_w"],
+                          eps=case.eps, theta=case.theta, stream=s)
+        d_out = gqa.decode(ddev["q"], ddev["k_cache"], ddev["v_cache"], ddev["seq_lens"],
+                           stream=s, **dkw)
+        junk = [torch.full((int(n),), 7.0, dtype=torch.bfloat16, device="cuda")
+                for n in (case.N * case.H * case.d, case.N * case.G * case.d,
+                          dcase.B * dcase.H * dcase.d, 1 << 22)]
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"prefill, repetition {rep}"
+        assert torch.equal(d_out, d_eager), f"decode, repetition {rep}"
+        del junk

@@ -38,8 +38,11 @@ MUTATIONS = [
     ("decode position one past the token", "pos = slot if position is None else int(position)",
      "pos = L if position is None else int(position)"),
     ("sampled rows ignore the causal mask",
-     "vis = visible_keys(1, e - s, causal, window, block_mask, block, q_index=[r])[0]",
-     "vis = visible_keys(1, e - s, False, window, block_mask, block, q_index=[r])[0]"),
+     "vis = visible_keys(len(r_in[c]), Tk, causal, window, block_mask, block,",
+     "vis = visible_keys(len(r_in[c]), Tk, False, window, block_mask, block,"),
+    ("sampled rows pair a head with another row's mask",
+     "S = np.where(np.repeat(vis, h, axis=0), S, -np.inf)",
+     "S = np.where(np.tile(vis, (h, 1)), S, -np.inf)"),
     ("cached positions restart at 0", "pos = (past + np.arange(e - s))", "pos = (np.arange(e - s))"),
     ("appended rows one slot late", "kc[b, past:past + e - s] = kt",
      "kc[b, past + 1:past + 1 + e - s] = kt"),
@@ -65,8 +68,8 @@ MUTATIONS = [
     ("block layout transposed", "vis &= bm[i // block, j // block] | (i // block == j // block)",
      "vis &= bm[j // block, i // block] | (i // block == j // block)"),
     ("sampled rows ignore the window",
-     "vis = visible_keys(1, e - s, causal, window, block_mask, block, q_index=[r])[0]",
-     "vis = visible_keys(1, e - s, causal, 0, block_mask, block, q_index=[r])[0]"),
+     "vis = visible_keys(len(r_in[c]), Tk, causal, window, block_mask, block,",
+     "vis = visible_keys(len(r_in[c]), Tk, causal, 0, block_mask, block,"),
 ]
 
 
