@@ -3,6 +3,7 @@
 // a rejected call enqueues nothing and touches no device.
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 #include <new>
 
 #include "gqa.h"
@@ -59,9 +60,19 @@ gqa_status check_heads(int H, int G, int d) {
   return GQA_OK;
 }
 
+// The dtype field as the caller stored it. A C caller may have put any int there, and
+// loading an enum object that holds a value outside the enumeration is undefined in C++, so
+// its bytes are read as an int; once this check passed, p->dtype holds GQA_F32 or GQA_BF16.
+int dtype_bits(const gqa_params* p) {
+  static_assert(sizeof(p->dtype) == sizeof(int), "gqa_dtype is int-sized");
+  int v;
+  std::memcpy(&v, &p->dtype, sizeof v);
+  return v;
+}
+
 gqa_status check_params(const gqa_params* p) {
   if (!p) return GQA_EINVAL;
-  if (!dtype_ok(p->dtype)) return GQA_ENOTSUP;
+  if (!dtype_ok(dtype_bits(p))) return GQA_ENOTSUP;
   if (!(p->eps >= 0.f) || !std::isfinite(p->eps)) return GQA_EINVAL;
   if (!(p->scale >= 0.f) || !std::isfinite(p->scale)) return GQA_EINVAL;
   if (!(p->rope_theta >= 0.0) || !std::isfinite(p->rope_theta)) return GQA_EINVAL;
