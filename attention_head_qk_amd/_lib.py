@@ -14,6 +14,7 @@ GQA_OK, GQA_EINVAL, GQA_ENOTSUP, GQA_EWORKSPACE, GQA_EHIP = range(5)
 GQA_F32, GQA_BF16 = 0, 1
 GQA_OP_PREFILL, GQA_OP_DECODE, GQA_OP_QK_NORM_ROPE = 0, 1, 2
 GQA_ROPE_BASE, GQA_ROPE_LINEAR, GQA_ROPE_YARN, GQA_ROPE_NTK = range(4)
+GQA_DECODE_NOALLOC_MAX_BYTES = 64 * 1024 * 1024
 
 # Every function include/gqa.h declares, with its ctypes signature.
 _vp = ctypes.c_void_p
@@ -51,6 +52,7 @@ SIGNATURES = {
     "gqa_prefill_cached": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                                 ctypes.POINTER(GqaParams)]),
     "gqa_decode": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.POINTER(GqaParams)]),
+    "gqa_decode_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.POINTER(GqaParams)]),
     "gqa_decode_graph_create": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
                                      ctypes.POINTER(GqaParams), ctypes.POINTER(_vp)]),
     "gqa_decode_graph_launch": (_i, [_vp, _vp]),

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "gqa.h"
@@ -222,6 +223,31 @@ gqa_status decode_enqueue(const void* q, void* k_cache, void* v_cache, const int
   if ((st = from_hip(gqa::launch_decode_split(da, d, bf16, stream))) != GQA_OK) return st;
   if (prof && (st = from_hip(mark(p->prof_stop, stream))) != GQA_OK) return st;
   return from_hip(gqa::launch_decode_combine(da, d, bf16, stream));
+}
+
+// ---- scratch of gqa_decode_noalloc: one fixed device array per GPU, so that entry point
+// allocates nothing. In host code `scratch` names a host-side stand-in, never the device
+// memory: its device address comes from hipGetSymbolAddress, taken once per device (with the
+// device current) on the first call there and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = (size_t)GQA_DECODE_NOALLOC_MAX_BYTES;
+__device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+gqa_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GQA_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return GQA_ENOTSUP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return GQA_EHIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return GQA_OK;
 }
 
 }  // namespace
@@ -504,6 +530,25 @@ gqa_status gqa_decode(const void* q, void* k_cache, void* v_cache, const int32_t
   if (st != GQA_OK || B == 0) return st;
   (void)hipGetLastError();
   return decode_enqueue(q, k_cache, v_cache, seq_lens, out, B, H, G, d, max_seq, p,
+                        reinterpret_cast<hipStream_t>(p->stream), true);
+}
+
+gqa_status gqa_decode_noalloc(const void* q, void* k_cache, void* v_cache,
+                              const int32_t* seq_lens, void* out, int B, int H, int G, int d,
+                              int max_seq, const gqa_params* p) {
+  if (!p) return GQA_EINVAL;
+  // every host check of gqa_decode, with the scratch array standing in for the workspace
+  // (a placeholder address until the checks pass, so a rejected call makes no HIP call)
+  gqa_params sp = *p;
+  sp.workspace = reinterpret_cast<void*>(kAlign);
+  sp.workspace_bytes = kScratchBytes;
+  gqa_status st = decode_check(q, k_cache, v_cache, seq_lens, out, B, H, G, d, max_seq, &sp);
+  if (st != GQA_OK || B == 0) return st;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != GQA_OK) return st;
+  sp.workspace = ws;
+  (void)hipGetLastError();
+  return decode_enqueue(q, k_cache, v_cache, seq_lens, out, B, H, G, d, max_seq, &sp,
                         reinterpret_cast<hipStream_t>(p->stream), true);
 }
 

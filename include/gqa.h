@@ -189,6 +189,26 @@ gqa_status gqa_decode(const void *q, void *k_cache, void *v_cache, const int32_t
                       void *out, int B, int H, int G, int d, int max_seq,
                       const gqa_params *p);
 
+/* gqa_decode without a workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, checks and result bits as gqa_decode; p->workspace and p->workspace_bytes are
+ * ignored.  The scratch (normalised queries, per-split partial results) lives instead in a
+ * fixed device array of GQA_DECODE_NOALLOC_MAX_BYTES inside the library, one per GPU, held
+ * from the first call on that GPU until the process ends; the call itself allocates nothing
+ * and calls no allocating routine.  GQA_EWORKSPACE when the decode needs more scratch than
+ * that (gqa_workspace_bytes(GQA_OP_DECODE, B, max_seq, H, G, d, dtype) above the maximum:
+ * e.g. 64 sequences x 32 heads over a 32768-row cache need 34.1 MB).  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (two streams, two threads, or
+ * one graph replay beside another call) race and give undefined results; calls ordered on
+ * one stream do not.  Nothing in the array needs clearing: each call writes every value
+ * it reads.  The first call on a GPU looks up the array's address (GQA_EHIP if that
+ * fails). */
+#define GQA_DECODE_NOALLOC_MAX_BYTES (64u * 1024u * 1024u)
+
+gqa_status gqa_decode_noalloc(const void *q, void *k_cache, void *v_cache,
+                              const int32_t *seq_lens, void *out, int B, int H, int G, int d,
+                              int max_seq, const gqa_params *p);
+
 /* Generation loop: the decode step captured once as a HIP graph and replayed per token.
  *   Generation runs one forward pass per new token, each seeing every earlier token
  *   (zhanghao0806.com page, D1-1, Q2 and Q5); the launches of one step are fixed, so they are

@@ -27,7 +27,8 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     for fn in ("gqa_prefill", "gqa_prefill_cached", "gqa_decode", "gqa_decode_graph_create",
                "gqa_decode_graph_launch", "gqa_decode_graph_destroy", "gqa_qk_norm_rope",
-               "gqa_workspace_bytes", "gqa_status_str", "gqa_params_init", "gqa_decode_split_keys"):
+               "gqa_workspace_bytes", "gqa_status_str", "gqa_params_init", "gqa_decode_split_keys",
+               "gqa_rope_freq_table", "gqa_decode_noalloc"):
         assert fn in names
 
 
@@ -184,6 +185,29 @@ def test_binding_shape_checks():
         gqa._block_mask_check(torch.zeros(130, 4, dtype=torch.int32), 130 * 64)  # 5 words needed
     with pytest.raises(ValueError):
         gqa._block_mask_check(torch.zeros(64, dtype=torch.int32), 64)
+
+
+def test_decode_noalloc_host_checks():
+    # the allocation-free decode makes every host check of gqa_decode (here with fake device
+    # addresses, so only rejections and the empty batch are called) and refuses decodes whose
+    # scratch would not fit its fixed array
+    lib = _lib.load()
+    f = lib.gqa_decode_noalloc
+    p = _lib.default_params()
+    sl = ctypes.c_void_p(A)
+    assert f(A, A, A, sl, A, 2, 6, 4, 128, 64, ctypes.byref(p)) == _lib.GQA_EINVAL   # H % G
+    assert f(A, A, A, sl, A, 2, 8, 8, 96, 64, ctypes.byref(p)) == _lib.GQA_ENOTSUP   # d
+    assert f(A, A, A, None, A, 2, 8, 8, 128, 64, ctypes.byref(p)) == _lib.GQA_EINVAL
+    assert f(MIS, A, A, sl, A, 2, 8, 8, 128, 64, ctypes.byref(p)) == _lib.GQA_EINVAL
+    assert f(A, A, A, sl, A, 0, 8, 8, 128, 64, ctypes.byref(p)) == _lib.GQA_OK       # no work
+    assert f(A, A, A, sl, A, 2, 8, 8, 128, 64, None) == _lib.GQA_EINVAL
+    need = lib.gqa_workspace_bytes(_lib.GQA_OP_DECODE, 64, 65536, 64, 8, 128, _lib.GQA_BF16)
+    assert need > _lib.GQA_DECODE_NOALLOC_MAX_BYTES
+    assert f(A, A, A, sl, A, 64, 64, 8, 128, 65536, ctypes.byref(p)) == _lib.GQA_EWORKSPACE
+    # p->workspace is ignored: a caller workspace that is too small changes nothing
+    p.workspace = ctypes.c_void_p(A)
+    p.workspace_bytes = 1
+    assert f(A, A, A, sl, A, 0, 8, 8, 128, 64, ctypes.byref(p)) == _lib.GQA_OK
 
 
 def test_status_strings():
