@@ -497,6 +497,9 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   const int d = threadIdx.x;
   const int L = a.seq_lens[b];
   const int ns = (L + a.split - 1) / a.split;
+  // generation-loop step: the step's lengths become the caller's (nothing else reads the
+  // caller's array during the step, so the copy can be made at any point of this pass)
+  if (a.lens_commit && head == 0 && d == 0) a.lens_commit[b] = L;
   const long base = ((long)b * a.H + head) * a.nsplit;
   T* out = reinterpret_cast<T*>(a.out) + ((long)b * a.H + head) * D + d;
   if (ns == 0) {
@@ -577,23 +580,6 @@ hipError_t launch_decode_split(const DecodeArgs& a, int d, bool bf16, hipStream_
   if (a.B <= 0) return hipSuccess;
   if (bf16) return d == 128 ? split_mfma_d<128>(a, s) : split_mfma_d<64>(a, s);
   return d == 128 ? split_td<float, 128>(a, s) : split_td<float, 64>(a, s);
-}
-
-// One step of a generation loop: every sequence gains the token about to be decoded (its
-// count stops at max_seq).
-__global__ __launch_bounds__(256) void seq_advance_kernel(int32_t* seq_lens, int B, int max_seq) {
-  const int b = blockIdx.x * 256 + threadIdx.x;
-  if (b < B) {
-    const int L = seq_lens[b];
-    seq_lens[b] = L < max_seq ? L + 1 : max_seq;
-  }
-}
-
-hipError_t launch_seq_advance(int32_t* seq_lens, int B, int max_seq, hipStream_t s) {
-  if (B <= 0) return hipSuccess;
-  hipLaunchKernelGGL(seq_advance_kernel, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, s,
-                     seq_lens, B, max_seq);
-  return hipGetLastError();
 }
 
 hipError_t launch_decode_combine(const DecodeArgs& a, int d, bool bf16, hipStream_t s) {

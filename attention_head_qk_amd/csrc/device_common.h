@@ -152,6 +152,9 @@ struct PrologueArgs {
   int max_seq;
   int use_rope;
   int slot0;          // first token slot of this launch (set by the launcher)
+  int32_t* lens_out;  // decode, generation-loop step: non-null = the sequence gains its new
+                      // token here (length min(seq_lens[b] + 1, max_seq)), and that length is
+                      // written to lens_out[b] for the rest of the step
   double omega[kMaxHalfD];  // theta^(-2j/d), computed on the host in fp64
 };
 
@@ -195,6 +198,8 @@ struct DecodeArgs {
   int split;          // keys per split, a multiple of 128 (4 waves x 32 keys)
   int stream_v;       // 1: V rows are read non-temporally (caches larger than the chip's caches)
   float scale_log2e;
+  int32_t* lens_commit;  // generation-loop step: the combine pass copies seq_lens[b] (the
+                         // step's own lengths) here at the end; null otherwise
 };
 
 constexpr int kDecodeSplit = 1024;       // longest split of the decode pass (keys)

@@ -166,10 +166,15 @@ gqa_status decode_check(const void* q, void* k_cache, void* v_cache, const int32
 }
 
 // The decode step's three launches (prologue with the optional append, split pass,
-// combine) on `stream`; `prof` records the caller's events around the split pass.
+// combine) on `stream`; `prof` records the caller's events around the split pass. With
+// `advance` (the generation-loop step) every sequence first gains its new token: the prologue
+// takes min(seq_lens[b] + 1, max_seq) as the length, hands it to the split and combine passes
+// through the workspace, and the combine pass writes it back into seq_lens -- no launch of its
+// own for the advance.
 gqa_status decode_enqueue(const void* q, void* k_cache, void* v_cache, const int32_t* seq_lens,
                           void* out, int B, int H, int G, int d, int max_seq,
-                          const gqa_params* p, hipStream_t stream, bool prof) {
+                          const gqa_params* p, hipStream_t stream, bool prof,
+                          bool advance = false) {
   gqa_status st;
   const bool bf16 = p->dtype == GQA_BF16;
   const size_t es = elem_size(p->dtype);
@@ -180,6 +185,8 @@ gqa_status decode_enqueue(const void* q, void* k_cache, void* v_cache, const int
   float* part_o = reinterpret_cast<float*>(ws + align_up((size_t)B * H * d * es));
   float* part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(part_o) +
                                             align_up((size_t)B * H * ns * d * 4));
+  int32_t* lens_ws = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(part_ml) +
+                                                align_up((size_t)B * H * ns * 2 * 4));
 
   gqa::PrologueArgs pa{};
   pa.q = q;
@@ -199,6 +206,7 @@ gqa_status decode_enqueue(const void* q, void* k_cache, void* v_cache, const int
   pa.H = H;
   pa.G = G;
   pa.max_seq = max_seq;
+  pa.lens_out = advance ? lens_ws : nullptr;
   fill_rope(pa, p, d);
   if ((st = from_hip(gqa::launch_prologue(pa, B, d, bf16, stream))) != GQA_OK) return st;
 
@@ -206,7 +214,8 @@ gqa_status decode_enqueue(const void* q, void* k_cache, void* v_cache, const int
   da.qt = qt;
   da.k_cache = k_cache;
   da.v_cache = v_cache;
-  da.seq_lens = seq_lens;
+  da.seq_lens = advance ? lens_ws : seq_lens;
+  da.lens_commit = advance ? const_cast<int32_t*>(seq_lens) : nullptr;
   da.part_o = part_o;
   da.part_ml = part_ml;
   da.out = out;
@@ -345,9 +354,11 @@ size_t gqa_workspace_bytes(int op, int B, int T_or_max_seq, int H, int G, int d,
     return (dtype == GQA_BF16 ? 0 : align_up(N * H * d * es)) + align_up(N * G * d * es);
   }
   if (op == GQA_OP_DECODE) {
+    // q~ [B, H, d], fp32 partial O [B, H, ns, d], (m, l) [B, H, ns, 2], and the lengths of
+    // a generation-loop step [B]
     const size_t ns = (size_t)decode_nsplit(B, H, G, T_or_max_seq);
     return align_up((size_t)B * H * d * es) + align_up((size_t)B * H * ns * d * 4) +
-           align_up((size_t)B * H * ns * 2 * 4);
+           align_up((size_t)B * H * ns * 2 * 4) + align_up((size_t)B * 4);
   }
   return 0;
 }
@@ -576,9 +587,9 @@ gqa_status gqa_decode_graph_create(const void* q, void* k_cache, void* v_cache,
     (void)hipStreamDestroy(cs);
     return GQA_EHIP;
   }
-  st = from_hip(gqa::launch_seq_advance(seq_lens, B, max_seq, cs));
-  if (st == GQA_OK && B > 0)
-    st = decode_enqueue(q, k_cache, v_cache, seq_lens, out, B, H, G, d, max_seq, p, cs, false);
+  if (B > 0)
+    st = decode_enqueue(q, k_cache, v_cache, seq_lens, out, B, H, G, d, max_seq, p, cs, false,
+                        /*advance=*/true);
   // the capture is ended whatever happened inside it
   const hipError_t ec = hipStreamEndCapture(cs, &g);
   if (st == GQA_OK && ec != hipSuccess) st = GQA_EHIP;

@@ -108,7 +108,10 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(PrologueArgs a) {
     k_tok_out = (long)bb * a.max_seq + past + t;
     if (r >= nq && past + t >= a.max_seq) active = false;
   } else {
-    const int L = len_in;
+    // a generation-loop step first gives the sequence its new token (capped at max_seq);
+    // one lane per sequence hands that length to the rest of the step
+    const int L = a.lens_out ? min(len_in + 1, a.max_seq) : len_in;
+    if (a.lens_out && active && r == 0 && ch == 0) a.lens_out[b] = L;
     pos = a.positions ? pos_in : (L > 0 ? L - 1 : 0);
     k_tok_out = (long)bb * a.max_seq + (L > 0 ? L - 1 : 0);
     if (r >= a.H && L == 0) active = false;  // nothing to append to an empty sequence

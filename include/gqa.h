@@ -217,9 +217,12 @@ gqa_status gqa_decode_noalloc(const void *q, void *k_cache, void *v_cache,
  *
  *   gqa_decode_graph_create takes the arguments of gqa_decode; p->k_new and p->v_new are
  *   required (every step appends its token).  It records, on a private stream, a step that
- *     1. sets seq_lens[b] = min(seq_lens[b] + 1, max_seq) for every b (device side), then
- *     2. does exactly what gqa_decode does with these arguments: norm + RoPE of q and k_new,
- *        k_new / v_new written at slot seq_lens[b] - 1, attention over seq_lens[b] rows.
+ *     1. gives every sequence its new token: L_b = min(seq_lens[b] + 1, max_seq) (device
+ *        side), then
+ *     2. does exactly what gqa_decode does with seq_lens[b] = L_b: norm + RoPE of q and
+ *        k_new, k_new / v_new written at slot L_b - 1, attention over L_b rows,
+ *   and leaves seq_lens[b] = L_b when the step has finished (the step's three kernels carry
+ *   the advance themselves: the prologue computes L_b, the last pass stores it).
  *   So before the first launch seq_lens[b] counts the tokens already in the cache.  Every
  *   pointer and size, and every field of *p except stream and the profiling events (which
  *   are ignored), is fixed at creation; the contents of q, k_new, v_new, positions and
