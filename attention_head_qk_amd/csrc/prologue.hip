@@ -75,6 +75,9 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(PrologueArgs a) {
     active = slot < a.B;
     tok = active ? slot : 0;
   }
+  // a packed batch launches max-length slots for every sequence: a wave whose slots all lie
+  // past their sequence's end (or past the last sequence) has nothing to do
+  if (!__any(active)) return;
   const int bb = active ? b : 0;
   const T* src;
   if (is_q) src = reinterpret_cast<const T*>(a.q) + ((long)tok * a.H + r) * D;

@@ -596,8 +596,25 @@ def bench_decode_loop(args, dev_name):
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / K
 
+    def gpu_only(fn):
+        """Per-step GPU time: the steps are queued behind a spin kernel long enough for the
+        host to enqueue all of them, so the events see the device run them back to back."""
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(max(20_000_000, K * 200_000))
+        a.record()
+        for i in range(K):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / K
+
     graph_ms = run(loop.replay)
     eager_ms = run(loop.eager)
+    graph_gpu_ms = gpu_only(loop.replay)
+    eager_gpu_ms = gpu_only(loop.eager)
     # the split-KV kernel alone, from the library's events around it in eager steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(K)]
@@ -607,16 +624,19 @@ def bench_decode_loop(args, dev_name):
     kern_ms = sum(a.elapsed_time(b) for a, b in ev) / K
     gbs = lambda ms: nbytes / K / (ms * 1e-3) / 1e9  # noqa: E731
     log(f"bench: decode loop graph {graph_ms * 1e3:.2f} us/step, eager {eager_ms * 1e3:.2f} "
-        f"us/step, split kernel {kern_ms * 1e3:.2f} us")
+        f"us/step (GPU only: graph {graph_gpu_ms * 1e3:.2f}, eager {eager_gpu_ms * 1e3:.2f}), "
+        f"split kernel {kern_ms * 1e3:.2f} us")
     line = {"metric": "decode loop GB/s (graph-replayed generation step)",
             "value": round(gbs(graph_ms), 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
             "warmup": args.warmup, "ms_per_step": round(graph_ms, 5), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "device": dev_name,
             "graph": {"us_per_step": round(graph_ms * 1e3, 3), "GB/s": round(gbs(graph_ms), 2),
-                      "tokens_per_s": round(c.B / (graph_ms * 1e-3), 1)},
+                      "tokens_per_s": round(c.B / (graph_ms * 1e-3), 1),
+                      "gpu_us_per_step": round(graph_gpu_ms * 1e3, 3)},
             "eager": {"us_per_step": round(eager_ms * 1e3, 3), "GB/s": round(gbs(eager_ms), 2),
-                      "tokens_per_s": round(c.B / (eager_ms * 1e-3), 1)},
+                      "tokens_per_s": round(c.B / (eager_ms * 1e-3), 1),
+                      "gpu_us_per_step": round(eager_gpu_ms * 1e3, 3)},
             "roofline": {"bound": "hbm", "achieved": round(gbs(kern_ms), 2),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs(kern_ms) / HBM_PEAK_GBS, 4),
