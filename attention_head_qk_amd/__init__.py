@@ -344,24 +344,42 @@ def decode(q, k_cache, v_cache, seq_lens, *, k_new=None, v_new=None, positions=N
 
 
 class DecodeGraph:
-    """gqa_decode_graph_*: one generation step captured once as a HIP graph.
+    """gqa_decode_graph_*: generation steps captured once as a HIP graph.
 
-    Each ``launch()`` first advances seq_lens[b] by one on the device (capped at max_seq), then
-    does what ``decode`` does with k_new / v_new: the new token's K/V are written at slot
+    Each step first advances seq_lens[b] by one on the device (capped at max_seq), then does
+    what ``decode`` does with k_new / v_new: the new token's K/V are written at slot
     seq_lens[b] - 1 and its query attends to seq_lens[b] rows; out receives the result. So
-    seq_lens starts at the number of tokens already cached. The tensors are bound at
-    creation: write the next step's q / k_new / v_new into them (in stream order) between
+    seq_lens starts at the number of tokens already cached. With ``steps`` > 1 one launch
+    runs that many steps (gqa_decode_graph_create_steps): q, out [steps, B, H, d], k_new,
+    v_new [steps, B, G, d], positions [steps, B], step i using block i. The tensors are bound
+    at creation: write the next tokens' q / k_new / v_new into them (in stream order) between
     launches. The object keeps references to every bound tensor; ``close()`` (or leaving a
     ``with`` block) waits for the device and releases the graph."""
 
     def __init__(self, q, k_cache, v_cache, seq_lens, k_new, v_new, *, positions=None,
                  q_norm_w=None, k_norm_w=None, eps=1e-6, theta=1e6, scale=0.0, out=None,
-                 workspace=None, rope_inv_freq=None):
+                 workspace=None, rope_inv_freq=None, steps=1):
         self._h = None
         for t, n in ((k_new, "k_new"), (v_new, "v_new")):
             if t is None:
                 raise ValueError(f"{n} is required")
-        B, H, G, d, S = _decode_shapes(q, k_cache, v_cache, seq_lens, k_new, v_new, positions)
+        steps = int(steps)
+        if steps < 1:
+            raise ValueError("steps must be >= 1")
+        if steps > 1:
+            # per-step blocks: check the whole tensors, then one block like a single step
+            _dev(q, "q")
+            if q.dim() != 4 or q.shape[0] != steps:
+                raise ValueError("with steps > 1, q is [steps, B, H, d]")
+            _dev(k_new, "k_new", q.dtype, (steps,) + tuple(k_new.shape[1:]))
+            _dev(v_new, "v_new", q.dtype, tuple(k_new.shape))
+            if positions is not None:
+                _dev(positions, "positions", torch.int32, (steps, q.shape[1]))
+            B, H, G, d, S = _decode_shapes(q[0], k_cache, v_cache, seq_lens, k_new[0], v_new[0],
+                                           None if positions is None else positions[0])
+        else:
+            B, H, G, d, S = _decode_shapes(q, k_cache, v_cache, seq_lens, k_new, v_new,
+                                           positions)
         dtype = q.dtype
         s = torch.cuda.current_stream(q.device)
         out = _out_like(out, q, "out", s)
@@ -377,14 +395,16 @@ class DecodeGraph:
         self._keep = (q, k_cache, v_cache, seq_lens, k_new, v_new, positions, q_norm_w,
                       k_norm_w, out, ws)
         h = ctypes.c_void_p()
-        rc = _lib.load().gqa_decode_graph_create(_ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                                 _ptr(seq_lens), _ptr(out), B, H, G, d, S,
-                                                 ctypes.byref(p), ctypes.byref(h))
-        _lib.check(rc, "gqa_decode_graph_create")
+        rc = _lib.load().gqa_decode_graph_create_steps(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                                       _ptr(seq_lens), _ptr(out), B, H, G, d,
+                                                       S, steps, ctypes.byref(p),
+                                                       ctypes.byref(h))
+        _lib.check(rc, "gqa_decode_graph_create_steps")
+        self.steps = steps
         self._h = h
 
     def launch(self, stream=None):
-        """Enqueue one step on ``stream`` (default: torch's current stream); returns out.
+        """Enqueue the step(s) on ``stream`` (default: torch's current stream); returns out.
         The bound tensors (out and the workspace included) belong to the stream the graph
         was created on: a launch on another stream must be ordered against that one by the
         caller."""

@@ -55,6 +55,8 @@ SIGNATURES = {
     "gqa_decode_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, ctypes.POINTER(GqaParams)]),
     "gqa_decode_graph_create": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
                                      ctypes.POINTER(GqaParams), ctypes.POINTER(_vp)]),
+    "gqa_decode_graph_create_steps": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
+                                           ctypes.POINTER(GqaParams), ctypes.POINTER(_vp)]),
     "gqa_decode_graph_launch": (_i, [_vp, _vp]),
     "gqa_decode_graph_destroy": (_i, [_vp]),
     "gqa_qk_norm_rope": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, ctypes.POINTER(GqaParams)]),

@@ -234,6 +234,9 @@ gqa_status decode_enqueue(const void* q, void* k_cache, void* v_cache, const int
   return from_hip(gqa::launch_decode_combine(da, d, bf16, stream));
 }
 
+// most decode steps one graph records
+constexpr int kMaxGraphSteps = 256;
+
 // ---- scratch of gqa_decode_noalloc: one fixed device array per GPU, so that entry point
 // allocates nothing. In host code `scratch` names a host-side stand-in, never the device
 // memory: its device address comes from hipGetSymbolAddress, taken once per device (with the
@@ -572,12 +575,23 @@ struct gqa_decode_graph {
 gqa_status gqa_decode_graph_create(const void* q, void* k_cache, void* v_cache,
                                    int32_t* seq_lens, void* out, int B, int H, int G, int d,
                                    int max_seq, const gqa_params* p, gqa_decode_graph** graph) {
+  return gqa_decode_graph_create_steps(q, k_cache, v_cache, seq_lens, out, B, H, G, d, max_seq,
+                                       1, p, graph);
+}
+
+gqa_status gqa_decode_graph_create_steps(const void* q, void* k_cache, void* v_cache,
+                                         int32_t* seq_lens, void* out, int B, int H, int G,
+                                         int d, int max_seq, int steps, const gqa_params* p,
+                                         gqa_decode_graph** graph) {
   if (!graph) return GQA_EINVAL;
   *graph = nullptr;
+  if (steps < 1 || steps > kMaxGraphSteps) return GQA_EINVAL;
   gqa_status st = decode_check(q, k_cache, v_cache, seq_lens, out, B, H, G, d, max_seq, p);
   if (st != GQA_OK) return st;
   if (!p->k_new || !p->v_new) return GQA_EINVAL;  // every step appends its token
   (void)hipGetLastError();
+  const size_t es = elem_size(p->dtype);
+  const size_t q_step = (size_t)B * H * d * es, kv_step = (size_t)B * G * d * es;
 
   hipStream_t cs = nullptr;
   if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return GQA_EHIP;
@@ -587,9 +601,17 @@ gqa_status gqa_decode_graph_create(const void* q, void* k_cache, void* v_cache,
     (void)hipStreamDestroy(cs);
     return GQA_EHIP;
   }
-  if (B > 0)
-    st = decode_enqueue(q, k_cache, v_cache, seq_lens, out, B, H, G, d, max_seq, p, cs, false,
-                        /*advance=*/true);
+  // step i reads its own q / k_new / v_new / positions rows and writes its own output rows;
+  // each step's kernels advance seq_lens for the next
+  for (int i = 0; i < steps && B > 0 && st == GQA_OK; ++i) {
+    gqa_params ps = *p;
+    ps.k_new = static_cast<const char*>(p->k_new) + i * kv_step;
+    ps.v_new = static_cast<const char*>(p->v_new) + i * kv_step;
+    if (p->positions) ps.positions = p->positions + (size_t)i * B;
+    st = decode_enqueue(static_cast<const char*>(q) + i * q_step, k_cache, v_cache, seq_lens,
+                        static_cast<char*>(out) + i * q_step, B, H, G, d, max_seq, &ps, cs,
+                        false, /*advance=*/true);
+  }
   // the capture is ended whatever happened inside it
   const hipError_t ec = hipStreamEndCapture(cs, &g);
   if (st == GQA_OK && ec != hipSuccess) st = GQA_EHIP;

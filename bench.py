@@ -537,7 +537,11 @@ class DecodeLoop:
     decodes one token per sequence (the new K/V appended first). The step's inputs are the
     workload's first-step tokens, bound once; every 64 steps seq_lens goes back to the
     starting cache lengths (one 64-byte device copy, inside the timed region), so each block of
-    64 steps repeats the workload's lengths."""
+    64 steps repeats the workload's lengths. Three ways to run it: eager gqa_decode calls, a
+    one-step graph replayed per token, and a graph of MULTI steps replayed per MULTI tokens
+    (a graph launch costs about 5 us more than stream launches, once per replay)."""
+
+    MULTI = 8
 
     def __init__(self, case):
         import attention_head_qk_amd as gqa
@@ -557,6 +561,14 @@ class DecodeLoop:
                        theta=c.theta)
         self.graph = gqa.DecodeGraph(self.q, self.kc, self.vc, self.sl, self.k, self.v,
                                      out=self.out, workspace=self.ws, **self.kw)
+        m = self.MULTI
+        assert c.S % m == 0
+        self.qm = self.q.unsqueeze(0).repeat(m, 1, 1, 1)
+        self.km = self.k.unsqueeze(0).repeat(m, 1, 1, 1)
+        self.vm = self.v.unsqueeze(0).repeat(m, 1, 1, 1)
+        self.outm = torch.empty_like(self.qm)
+        self.graph_m = gqa.DecodeGraph(self.qm, self.kc, self.vc, self.sl, self.km, self.vm,
+                                       out=self.outm, workspace=self.ws, steps=m, **self.kw)
 
     def eager(self, i, prof=None):
         if i % self.case.S == 0:
@@ -569,6 +581,14 @@ class DecodeLoop:
         if i % self.case.S == 0:
             self.sl.copy_(self.sl0)
         self.graph.launch()
+
+    def replay_multi(self, i):
+        """Steps i .. i + MULTI - 1 in one launch (called for every i, launches at multiples)."""
+        if i % self.MULTI:
+            return
+        if i % self.case.S == 0:
+            self.sl.copy_(self.sl0)
+        self.graph_m.launch()
 
     def step_bytes(self, i):
         """Algorithmic bytes of step i: the K and V rows it sees, plus q in and out."""
@@ -583,11 +603,14 @@ def bench_decode_loop(args, dev_name):
     loop = DecodeLoop(W.decode_loop())
     c = loop.case
     log(f"bench: decode loop inputs ready ({c.name})")
-    K = args.steps
+    # whole launches of the multi-step graph: steps and warmup rounded up to multiples of MULTI
+    m = loop.MULTI
+    K = -(-args.steps // m) * m
+    warm = -(-args.warmup // m) * m
     nbytes = sum(loop.step_bytes(i) for i in range(K))
 
     def run(fn):
-        for i in range(args.warmup):
+        for i in range(warm):
             fn(i)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -599,7 +622,7 @@ def bench_decode_loop(args, dev_name):
     def gpu_only(fn):
         """Per-step GPU time: the steps are queued behind a spin kernel long enough for the
         host to enqueue all of them, so the events see the device run them back to back."""
-        for i in range(args.warmup):
+        for i in range(warm):
             fn(i)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -612,8 +635,10 @@ def bench_decode_loop(args, dev_name):
         return a.elapsed_time(b) / K
 
     graph_ms = run(loop.replay)
+    multi_ms = run(loop.replay_multi)
     eager_ms = run(loop.eager)
     graph_gpu_ms = gpu_only(loop.replay)
+    multi_gpu_ms = gpu_only(loop.replay_multi)
     eager_gpu_ms = gpu_only(loop.eager)
     # the split-KV kernel alone, from the library's events around it in eager steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -623,14 +648,20 @@ def bench_decode_loop(args, dev_name):
     torch.cuda.synchronize()
     kern_ms = sum(a.elapsed_time(b) for a, b in ev) / K
     gbs = lambda ms: nbytes / K / (ms * 1e-3) / 1e9  # noqa: E731
-    log(f"bench: decode loop graph {graph_ms * 1e3:.2f} us/step, eager {eager_ms * 1e3:.2f} "
-        f"us/step (GPU only: graph {graph_gpu_ms * 1e3:.2f}, eager {eager_gpu_ms * 1e3:.2f}), "
-        f"split kernel {kern_ms * 1e3:.2f} us")
-    line = {"metric": "decode loop GB/s (graph-replayed generation step)",
-            "value": round(gbs(graph_ms), 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
-            "warmup": args.warmup, "ms_per_step": round(graph_ms, 5), "higher_is_better": True,
+    log(f"bench: decode loop graph {graph_ms * 1e3:.2f} us/step, {loop.MULTI}-step graph "
+        f"{multi_ms * 1e3:.2f}, eager {eager_ms * 1e3:.2f} us/step (GPU only: graph "
+        f"{graph_gpu_ms * 1e3:.2f}, {loop.MULTI}-step graph {multi_gpu_ms * 1e3:.2f}, eager "
+        f"{eager_gpu_ms * 1e3:.2f}), split kernel {kern_ms * 1e3:.2f} us")
+    line = {"metric": f"decode loop GB/s (generation steps replayed {loop.MULTI} per HIP graph)",
+            "value": round(gbs(multi_ms), 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+            "warmup": warm, "ms_per_step": round(multi_ms, 5), "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
             "device": dev_name,
+            "graph_multi": {"steps_per_launch": loop.MULTI,
+                            "us_per_step": round(multi_ms * 1e3, 3),
+                            "GB/s": round(gbs(multi_ms), 2),
+                            "tokens_per_s": round(c.B / (multi_ms * 1e-3), 1),
+                            "gpu_us_per_step": round(multi_gpu_ms * 1e3, 3)},
             "graph": {"us_per_step": round(graph_ms * 1e3, 3), "GB/s": round(gbs(graph_ms), 2),
                       "tokens_per_s": round(c.B / (graph_ms * 1e-3), 1),
                       "gpu_us_per_step": round(graph_gpu_ms * 1e3, 3)},
@@ -647,6 +678,7 @@ def bench_decode_loop(args, dev_name):
                        "G": c.G, "d": c.d, "seed": c.seed},
             "cpu_baseline": None}
     loop.graph.close()
+    loop.graph_m.close()
     print(json.dumps(line), flush=True)
     return 0
 

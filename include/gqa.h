@@ -235,7 +235,8 @@ gqa_status gqa_decode_noalloc(const void *q, void *k_cache, void *v_cache,
  *   object holds the instantiated HIP graph (no device memory of the library's own).
  *   B == 0 gives a graph whose launches do nothing.
  *
- *   gqa_decode_graph_launch enqueues one step on `stream` (a hipStream_t; NULL = default).
+ *   gqa_decode_graph_launch enqueues the graph's step(s) on `stream` (a hipStream_t; NULL =
+ *   default).
  *   Launches on one graph must not overlap (they share the workspace); in one stream they
  *   never do.
  *   gqa_decode_graph_destroy releases the graph (NULL is accepted); its launches must have
@@ -245,6 +246,19 @@ typedef struct gqa_decode_graph gqa_decode_graph;
 gqa_status gqa_decode_graph_create(const void *q, void *k_cache, void *v_cache,
                                    int32_t *seq_lens, void *out, int B, int H, int G, int d,
                                    int max_seq, const gqa_params *p, gqa_decode_graph **graph);
+
+/* Several generation steps in one graph (a HIP graph launch costs about 5 us more than the
+ * stream launches of its kernels, measured on MI355X, so a graph of several steps spends it
+ * once per `steps` tokens).  Arguments as gqa_decode_graph_create, with 1 <= steps <= 256
+ * (else GQA_EINVAL): q and out hold `steps` consecutive [B, H, d] blocks, p->k_new and
+ * p->v_new `steps` consecutive [B, G, d] blocks, p->positions (when set) `steps` consecutive
+ * [B] blocks; step i reads and writes block i.  One launch runs the steps in order, each
+ * doing what one launch of a one-step graph does (so seq_lens[b] grows by `steps`, capped at
+ * max_seq).  gqa_decode_graph_create is this function with steps = 1. */
+gqa_status gqa_decode_graph_create_steps(const void *q, void *k_cache, void *v_cache,
+                                         int32_t *seq_lens, void *out, int B, int H, int G,
+                                         int d, int max_seq, int steps, const gqa_params *p,
+                                         gqa_decode_graph **graph);
 
 gqa_status gqa_decode_graph_launch(gqa_decode_graph *graph, void *stream);
 

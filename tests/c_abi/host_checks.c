@@ -100,6 +100,11 @@ int main(void) {
   EXPECT(g == NULL);
   EXPECT(gqa_decode_graph_create(A, A, A, (int32_t *)IA, A, 2, 8, 8, 128, 64, &p, NULL) ==
          GQA_EINVAL);
+  EXPECT(gqa_decode_graph_create_steps(A, A, A, (int32_t *)IA, A, 2, 8, 8, 128, 64, 0, &p, &g) ==
+         GQA_EINVAL); /* steps < 1 */
+  EXPECT(gqa_decode_graph_create_steps(A, A, A, (int32_t *)IA, A, 2, 8, 8, 128, 64, 257, &p, &g) ==
+         GQA_EINVAL); /* steps > 256 */
+  EXPECT(g == NULL);
   EXPECT(gqa_decode_graph_launch(NULL, NULL) == GQA_EINVAL);
   EXPECT(gqa_decode_graph_destroy(NULL) == GQA_OK);
 

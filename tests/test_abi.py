@@ -28,7 +28,7 @@ def test_header_declares_expected_entry_points():
     for fn in ("gqa_prefill", "gqa_prefill_cached", "gqa_decode", "gqa_decode_graph_create",
                "gqa_decode_graph_launch", "gqa_decode_graph_destroy", "gqa_qk_norm_rope",
                "gqa_workspace_bytes", "gqa_status_str", "gqa_params_init", "gqa_decode_split_keys",
-               "gqa_rope_freq_table", "gqa_decode_noalloc"):
+               "gqa_rope_freq_table", "gqa_decode_noalloc", "gqa_decode_graph_create_steps"):
         assert fn in names
 
 
@@ -357,13 +357,18 @@ def test_prefill_cached_rejects_before_launch(kw, code):
 
 
 def _graph_create(q=A, kc=A, vc=A, sl=A, out=A, B=2, H=4, G=2, d=128, S=16, out_handle=True,
-                  **kw):
+                  steps=None, **kw):
     kw.setdefault("k_new", A)
     kw.setdefault("v_new", A)
     p = _params(**kw)
     h = ctypes.c_void_p()
-    rc = _lib.load().gqa_decode_graph_create(q, kc, vc, sl, out, B, H, G, d, S, ctypes.byref(p),
-                                             ctypes.byref(h) if out_handle else None)
+    hp = ctypes.byref(h) if out_handle else None
+    if steps is None:
+        rc = _lib.load().gqa_decode_graph_create(q, kc, vc, sl, out, B, H, G, d, S,
+                                                 ctypes.byref(p), hp)
+    else:
+        rc = _lib.load().gqa_decode_graph_create_steps(q, kc, vc, sl, out, B, H, G, d, S, steps,
+                                                       ctypes.byref(p), hp)
     assert not h.value  # nothing is created on a rejected call
     return rc
 
@@ -376,6 +381,9 @@ def _graph_create(q=A, kc=A, vc=A, sl=A, out=A, B=2, H=4, G=2, d=128, S=16, out_
     (dict(S=0), _lib.GQA_EINVAL), (dict(H=5, G=2), _lib.GQA_EINVAL),
     (dict(d=96), _lib.GQA_ENOTSUP), (dict(workspace_bytes=10), _lib.GQA_EWORKSPACE),
     (dict(positions=A + 2), _lib.GQA_EINVAL), (dict(B=-1), _lib.GQA_EINVAL),
+    (dict(steps=0), _lib.GQA_EINVAL), (dict(steps=257), _lib.GQA_EINVAL),
+    (dict(steps=-3), _lib.GQA_EINVAL), (dict(steps=8, k_new=None), _lib.GQA_EINVAL),
+    (dict(steps=8, d=96), _lib.GQA_ENOTSUP), (dict(steps=2, workspace_bytes=10), _lib.GQA_EWORKSPACE),
 ])
 def test_decode_graph_create_rejects_before_any_hip_call(kw, code):
     assert _graph_create(**kw) == code

@@ -138,3 +138,38 @@ def test_graph_full_cache_stays_at_max_seq():
     g.close()
     assert sl.tolist() == [64, 13]
     assert not torch.isnan(kc.float()).any()
+
+
+@pytest.mark.parametrize("per", [4, 6])
+def test_multi_step_graph_equals_eager(per):
+    # gqa_decode_graph_create_steps: `per` steps per launch over [per, B, ...] blocks; two
+    # launches (the second with new inputs written between them) equal 2 * per eager steps bit
+    # for bit, caches and lengths included
+    import attention_head_qk_amd as gqa
+    S = 2 * per
+    case = W.make_decode_steps(f"graph_multi{per}", 113 + per, [0, 900, 1023, 2080, 5], S,
+                               2096, H=32, G=8, d=128)
+    dev = device_steps_inputs(case)
+    say("multi-step decode graph", per)
+    want_out, want_kc, want_vc, want_sl = _eager_steps(case, dev)
+    kc, vc, sl = dev["k_cache"].clone(), dev["v_cache"].clone(), dev["seq_lens"].clone()
+    q = torch.empty((per,) + tuple(dev["q"].shape[1:]), dtype=dev["q"].dtype, device="cuda")
+    k = torch.empty((per,) + tuple(dev["k"].shape[1:]), dtype=dev["k"].dtype, device="cuda")
+    v = torch.empty_like(k)
+    g = gqa.DecodeGraph(q, kc, vc, sl, k, v, q_norm_w=dev["q_norm_w"], k_norm_w=dev["k_norm_w"],
+                        eps=case.eps, theta=case.theta, steps=per)
+    with g:
+        for rep in range(2):
+            blk = slice(rep * per, (rep + 1) * per)
+            q.copy_(dev["q"][blk])
+            k.copy_(dev["k"][blk])
+            v.copy_(dev["v"][blk])
+            out = g.launch().clone()
+            torch.cuda.synchronize()
+            assert torch.equal(out, want_out[blk]), f"launch {rep}"
+            assert torch.equal(sl, dev["seq_lens"] + (rep + 1) * per)
+    assert torch.equal(kc, want_kc) and torch.equal(vc, want_vc) and torch.equal(sl, want_sl)
+    o_out, _, _ = oracle_decode_steps(case)
+    got = to_f64(want_out)
+    for s in range(S):
+        check(got[s], o_out[s], W.BF16, f"step {s}")
