@@ -165,18 +165,16 @@ gqa_status decode_check(const void* q, void* k_cache, void* v_cache, const int32
   return GQA_OK;
 }
 
-// The decode step's three launches (prologue with the optional append, split pass,
-// combine) on `stream`; `prof` records the caller's events around the split pass. With
-// `advance` (the generation-loop step) every sequence first gains its new token: the prologue
-// takes min(seq_lens[b] + 1, max_seq) as the length, hands it to the split and combine passes
-// through the workspace, and the combine pass writes it back into seq_lens -- no launch of its
-// own for the advance.
-gqa_status decode_enqueue(const void* q, void* k_cache, void* v_cache, const int32_t* seq_lens,
-                          void* out, int B, int H, int G, int d, int max_seq,
-                          const gqa_params* p, hipStream_t stream, bool prof,
-                          bool advance = false) {
-  gqa_status st;
-  const bool bf16 = p->dtype == GQA_BF16;
+// The kernel arguments of one decode step (prologue with the optional append; split and
+// combine passes). With `advance` (a generation-loop step) every sequence first gains its new
+// token: the prologue takes min(len_in[b] + 1, max_seq) as the length and writes it to
+// lens_step, the split and combine passes read it there, and the combine pass copies it into
+// seq_lens -- no launch of its own for the advance. len_in is seq_lens, or the previous
+// step's lens_step inside a multi-step graph.
+void decode_args(const void* q, void* k_cache, void* v_cache, const int32_t* seq_lens,
+                 void* out, int B, int H, int G, int d, int max_seq, const gqa_params* p,
+                 bool advance, const int32_t* len_in, int32_t* lens_step, gqa::PrologueArgs& pa,
+                 gqa::DecodeArgs& da) {
   const size_t es = elem_size(p->dtype);
   const int split = decode_split_len(B, H, G, max_seq);
   const int ns = decode_nsplit(B, H, G, max_seq);
@@ -185,10 +183,8 @@ gqa_status decode_enqueue(const void* q, void* k_cache, void* v_cache, const int
   float* part_o = reinterpret_cast<float*>(ws + align_up((size_t)B * H * d * es));
   float* part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(part_o) +
                                             align_up((size_t)B * H * ns * d * 4));
-  int32_t* lens_ws = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(part_ml) +
-                                                align_up((size_t)B * H * ns * 2 * 4));
 
-  gqa::PrologueArgs pa{};
+  pa = gqa::PrologueArgs{};
   pa.q = q;
   pa.k = p->k_new;
   pa.v = p->v_new;
@@ -196,7 +192,7 @@ gqa_status decode_enqueue(const void* q, void* k_cache, void* v_cache, const int
   pa.k_out = k_cache;
   pa.v_out = v_cache;
   pa.positions = p->positions;
-  pa.seq_lens = seq_lens;
+  pa.seq_lens = advance ? len_in : seq_lens;
   pa.gq = p->q_norm_w;
   pa.gk = p->k_norm_w;
   pa.eps = p->eps;
@@ -206,15 +202,14 @@ gqa_status decode_enqueue(const void* q, void* k_cache, void* v_cache, const int
   pa.H = H;
   pa.G = G;
   pa.max_seq = max_seq;
-  pa.lens_out = advance ? lens_ws : nullptr;
+  pa.lens_out = advance ? lens_step : nullptr;
   fill_rope(pa, p, d);
-  if ((st = from_hip(gqa::launch_prologue(pa, B, d, bf16, stream))) != GQA_OK) return st;
 
-  gqa::DecodeArgs da{};
+  da = gqa::DecodeArgs{};
   da.qt = qt;
   da.k_cache = k_cache;
   da.v_cache = v_cache;
-  da.seq_lens = advance ? lens_ws : seq_lens;
+  da.seq_lens = advance ? lens_step : seq_lens;
   da.lens_commit = advance ? const_cast<int32_t*>(seq_lens) : nullptr;
   da.part_o = part_o;
   da.part_ml = part_ml;
@@ -228,10 +223,74 @@ gqa_status decode_enqueue(const void* q, void* k_cache, void* v_cache, const int
   da.split = split;
   da.stream_v = 2.0 * B * max_seq * G * d * (double)es > kDecodeStreamBytes;
   da.scale_log2e = (float)((double)eff_scale(p, d) * 1.4426950408889634074);
+}
+
+// The two per-step length buffers of the decode workspace (after q~ and the partials):
+// a multi-step graph alternates between them, a single step uses the first.
+int32_t* decode_lens_ws(const gqa_params* p, int B, int H, int G, int d, int max_seq, int which) {
+  const size_t es = elem_size(p->dtype);
+  const int ns = decode_nsplit(B, H, G, max_seq);
+  char* ws = static_cast<char*>(p->workspace);
+  const size_t off = align_up((size_t)B * H * d * es) + align_up((size_t)B * H * ns * d * 4) +
+                     align_up((size_t)B * H * ns * 2 * 4) + (size_t)which * align_up((size_t)B * 4);
+  return reinterpret_cast<int32_t*>(ws + off);
+}
+
+// The decode step's three launches on `stream`; `prof` records the caller's events around the
+// split pass; `advance` as in decode_args.
+gqa_status decode_enqueue(const void* q, void* k_cache, void* v_cache, const int32_t* seq_lens,
+                          void* out, int B, int H, int G, int d, int max_seq,
+                          const gqa_params* p, hipStream_t stream, bool prof,
+                          bool advance = false) {
+  gqa_status st;
+  const bool bf16 = p->dtype == GQA_BF16;
+  gqa::PrologueArgs pa;
+  gqa::DecodeArgs da;
+  decode_args(q, k_cache, v_cache, seq_lens, out, B, H, G, d, max_seq, p, advance, seq_lens,
+              decode_lens_ws(p, B, H, G, d, max_seq, 0), pa, da);
+  if ((st = from_hip(gqa::launch_prologue(pa, B, d, bf16, stream))) != GQA_OK) return st;
   if (prof && (st = from_hip(mark(p->prof_start, stream))) != GQA_OK) return st;
   if ((st = from_hip(gqa::launch_decode_split(da, d, bf16, stream))) != GQA_OK) return st;
   if (prof && (st = from_hip(mark(p->prof_stop, stream))) != GQA_OK) return st;
   return from_hip(gqa::launch_decode_combine(da, d, bf16, stream));
+}
+
+// `steps` generation-loop steps (multi-step decode graph): step i reads and writes its own
+// input and output blocks. Between two steps one launch runs step i's combine beside step
+// i + 1's prologue (their data are disjoint; see the fused kernel), so a graph of S steps is
+// 2 S + 1 kernels. The step lengths alternate between the two workspace buffers: step i + 1's
+// prologue reads step i's lengths from one while writing its own to the other.
+gqa_status decode_steps_enqueue(const void* q, void* k_cache, void* v_cache, int32_t* seq_lens,
+                                void* out, int B, int H, int G, int d, int max_seq, int steps,
+                                const gqa_params* p, hipStream_t stream) {
+  gqa_status st;
+  const bool bf16 = p->dtype == GQA_BF16;
+  const size_t es = elem_size(p->dtype);
+  const size_t q_step = (size_t)B * H * d * es, kv_step = (size_t)B * G * d * es;
+  int32_t* lens[2] = {decode_lens_ws(p, B, H, G, d, max_seq, 0),
+                      decode_lens_ws(p, B, H, G, d, max_seq, 1)};
+  auto step_args = [&](int i, gqa::PrologueArgs& pa, gqa::DecodeArgs& da) {
+    gqa_params ps = *p;
+    ps.k_new = static_cast<const char*>(p->k_new) + i * kv_step;
+    ps.v_new = static_cast<const char*>(p->v_new) + i * kv_step;
+    if (p->positions) ps.positions = p->positions + (size_t)i * B;
+    decode_args(static_cast<const char*>(q) + i * q_step, k_cache, v_cache, seq_lens,
+                static_cast<char*>(out) + i * q_step, B, H, G, d, max_seq, &ps, true,
+                i == 0 ? seq_lens : lens[(i - 1) & 1], lens[i & 1], pa, da);
+  };
+  gqa::PrologueArgs pa, pn;
+  gqa::DecodeArgs da, dn;
+  step_args(0, pa, da);
+  if ((st = from_hip(gqa::launch_prologue(pa, B, d, bf16, stream))) != GQA_OK) return st;
+  for (int i = 0; i < steps; ++i) {
+    if ((st = from_hip(gqa::launch_decode_split(da, d, bf16, stream))) != GQA_OK) return st;
+    if (i + 1 == steps) return from_hip(gqa::launch_decode_combine(da, d, bf16, stream));
+    step_args(i + 1, pn, dn);
+    if ((st = from_hip(gqa::launch_decode_combine_prologue(da, pn, d, bf16, stream))) != GQA_OK)
+      return st;
+    da = dn;
+  }
+  return GQA_OK;
 }
 
 // most decode steps one graph records
@@ -361,7 +420,7 @@ size_t gqa_workspace_bytes(int op, int B, int T_or_max_seq, int H, int G, int d,
     // a generation-loop step [B]
     const size_t ns = (size_t)decode_nsplit(B, H, G, T_or_max_seq);
     return align_up((size_t)B * H * d * es) + align_up((size_t)B * H * ns * d * 4) +
-           align_up((size_t)B * H * ns * 2 * 4) + align_up((size_t)B * 4);
+           align_up((size_t)B * H * ns * 2 * 4) + 2 * align_up((size_t)B * 4);
   }
   return 0;
 }
@@ -601,16 +660,22 @@ gqa_status gqa_decode_graph_create_steps(const void* q, void* k_cache, void* v_c
     (void)hipStreamDestroy(cs);
     return GQA_EHIP;
   }
-  // step i reads its own q / k_new / v_new / positions rows and writes its own output rows;
-  // each step's kernels advance seq_lens for the next
-  for (int i = 0; i < steps && B > 0 && st == GQA_OK; ++i) {
-    gqa_params ps = *p;
-    ps.k_new = static_cast<const char*>(p->k_new) + i * kv_step;
-    ps.v_new = static_cast<const char*>(p->v_new) + i * kv_step;
-    if (p->positions) ps.positions = p->positions + (size_t)i * B;
-    st = decode_enqueue(static_cast<const char*>(q) + i * q_step, k_cache, v_cache, seq_lens,
-                        static_cast<char*>(out) + i * q_step, B, H, G, d, max_seq, &ps, cs,
-                        false, /*advance=*/true);
+  if (B > 0) {
+    // one step: its three kernels; several: 2 steps + 1 kernels with the fused passes between
+    // steps (while the prologue rows of one launch stay below 2^22)
+    if (steps == 1 || (long)B * (H + 2L * G) >= (1L << 22))
+      for (int i = 0; i < steps && st == GQA_OK; ++i) {
+        gqa_params ps = *p;
+        ps.k_new = static_cast<const char*>(p->k_new) + i * kv_step;
+        ps.v_new = static_cast<const char*>(p->v_new) + i * kv_step;
+        if (p->positions) ps.positions = p->positions + (size_t)i * B;
+        st = decode_enqueue(static_cast<const char*>(q) + i * q_step, k_cache, v_cache, seq_lens,
+                            static_cast<char*>(out) + i * q_step, B, H, G, d, max_seq, &ps, cs,
+                            false, /*advance=*/true);
+      }
+    else
+      st = decode_steps_enqueue(q, k_cache, v_cache, seq_lens, out, B, H, G, d, max_seq, steps,
+                                p, cs);
   }
   // the capture is ended whatever happened inside it
   const hipError_t ec = hipStreamEndCapture(cs, &g);

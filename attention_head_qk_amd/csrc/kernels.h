@@ -18,5 +18,9 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, int d, hipStream_t s);
 // decode split-KV pass, then the cross-split combine pass.
 hipError_t launch_decode_split(const DecodeArgs& a, int d, bool bf16, hipStream_t s);
 hipError_t launch_decode_combine(const DecodeArgs& a, int d, bool bf16, hipStream_t s);
+// decode graph of several steps: step n's combine and step n + 1's prologue (with its K/V
+// append) in one launch; the prologue's slots are the B sequences (pa.decode == 1)
+hipError_t launch_decode_combine_prologue(const DecodeArgs& ca, const PrologueArgs& pa, int d,
+                                          bool bf16, hipStream_t s);
 
 }  // namespace gqa

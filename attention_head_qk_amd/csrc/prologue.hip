@@ -14,6 +14,7 @@
 // attention kernel prepares Q itself) only K rows are processed.
 #include <algorithm>
 
+#include "decode_combine.h"
 #include "device_common.h"
 #include "kernels.h"
 
@@ -39,14 +40,17 @@ __device__ __forceinline__ float lane_group_sum(float v) {
 
 }  // namespace
 
+// The rows of one 256-thread block `blk` of the prologue grid; thread `tid` of it. (The fused
+// combine + prologue pass of a multi-step decode graph runs these blocks as D-thread pieces:
+// nothing here synchronises beyond a wave.)
 template <typename T, int D>
-__global__ __launch_bounds__(256) void qk_norm_rope_kernel(PrologueArgs a) {
+__device__ __forceinline__ void prologue_block(const PrologueArgs& a, unsigned blk, unsigned tid) {
   constexpr int LPR = D / 8;  // lanes per head row (8 elements = one 16-byte bf16 chunk each)
   const int nq = a.q ? a.H : 0, nk = a.k ? a.G : 0;
   const int rows_per_token = nq + nk + ((a.decode && a.v) ? a.G : 0);
   // (token slot, row) of this lane's row; the launcher keeps slots * rows below 2^31
-  const unsigned item = blockIdx.x * (256u / LPR) + threadIdx.x / LPR;
-  const int ch = threadIdx.x % LPR;
+  const unsigned item = blk * (256u / LPR) + tid / LPR;
+  const int ch = tid % LPR;
   const int e0 = ch * 8;
   const int slot = a.slot0 + (int)(item / (unsigned)rows_per_token);
   const int r = (int)(item % (unsigned)rows_per_token);
@@ -153,6 +157,33 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(PrologueArgs a) {
 }
 
 template <typename T, int D>
+__global__ __launch_bounds__(256) void qk_norm_rope_kernel(PrologueArgs a) {
+  prologue_block<T, D>(a, blockIdx.x, threadIdx.x);
+}
+
+// A multi-step decode graph's pass between two steps: blocks [0, n_comb) merge step n's splits
+// (one (sequence, head) each, D threads), the rest run step n + 1's prologue (its norm, RoPE
+// and K/V append), each 256-thread prologue block as 256 / D consecutive blocks. The two
+// jobs touch disjoint data (the combine reads the split partials and step n's lengths and
+// writes out; the prologue reads step n's lengths and writes q~, the cache rows and step
+// n + 1's lengths), so one launch runs them side by side.
+template <typename T, int D>
+__global__ __launch_bounds__(D) void decode_combine_prologue_kernel(DecodeArgs ca, PrologueArgs pa,
+                                                                    int n_comb) {
+  __shared__ float sw[kMaxCombineSplits];
+  __shared__ float s_inv;
+  const unsigned bx = blockIdx.x;
+  if (bx < (unsigned)n_comb) {
+    combine_one<T, D>(ca, (int)(bx % (unsigned)ca.H), (int)(bx / (unsigned)ca.H), threadIdx.x, sw,
+                      s_inv);
+    return;
+  }
+  constexpr unsigned PIECES = 256 / D;
+  const unsigned v = bx - (unsigned)n_comb;
+  prologue_block<T, D>(pa, v / PIECES, (v % PIECES) * D + threadIdx.x);
+}
+
+template <typename T, int D>
 static hipError_t launch_prologue_t(const PrologueArgs& a, int slots, hipStream_t s) {
   constexpr int ROWS_PER_BLOCK = 256 / (D / 8);
   const long rpt = (a.q ? a.H : 0) + (a.k ? a.G : 0) + ((a.decode && a.v) ? a.G : 0);
@@ -170,6 +201,27 @@ static hipError_t launch_prologue_t(const PrologueArgs& a, int slots, hipStream_
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+template <typename T, int D>
+static hipError_t launch_combine_prologue_t(const DecodeArgs& ca, const PrologueArgs& pa,
+                                            hipStream_t s) {
+  constexpr int ROWS_PER_BLOCK = 256 / (D / 8);
+  const long rpt = pa.H + 2L * pa.G;  // q, k_new and v_new rows of every sequence
+  const long pblocks = (pa.B * rpt + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
+  const long grid = (long)ca.H * ca.B + pblocks * (256 / D);
+  hipLaunchKernelGGL((decode_combine_prologue_kernel<T, D>), dim3((unsigned)grid), dim3(D), 0, s,
+                     ca, pa, ca.H * ca.B);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_combine_prologue(const DecodeArgs& ca, const PrologueArgs& pa, int d,
+                                          bool bf16, hipStream_t s) {
+  if (ca.B <= 0) return hipSuccess;
+  if (bf16) return d == 128 ? launch_combine_prologue_t<bf16_t, 128>(ca, pa, s)
+                            : launch_combine_prologue_t<bf16_t, 64>(ca, pa, s);
+  return d == 128 ? launch_combine_prologue_t<float, 128>(ca, pa, s)
+                  : launch_combine_prologue_t<float, 64>(ca, pa, s);
 }
 
 hipError_t launch_prologue(const PrologueArgs& a, int slots, int d, bool bf16, hipStream_t s) {

@@ -231,11 +231,11 @@ def test_workspace_bytes():
     assert ws(_lib.GQA_OP_PREFILL, 1, 4096, 16, 8, 128, _lib.GQA_BF16) == 4096 * 8 * 128 * 2
     assert ws(_lib.GQA_OP_PREFILL, 1, 3, 2, 1, 64, _lib.GQA_F32) == 1536 + 768
     assert ws(_lib.GQA_OP_PREFILL, 1, 3, 1, 1, 64, _lib.GQA_BF16) == 512  # 384 -> 512
-    # decode: q~ + fp32 partial O + fp32 (m, l) per split
+    # decode: q~ + fp32 partial O + fp32 (m, l) per split + two [B] step-length buffers
     S = lib.gqa_decode_split_keys(64, 32, 8, 32768)
     assert S == 1024
     ns = -(-32768 // S)
-    want = 64 * 32 * 128 * 2 + 64 * 32 * ns * 128 * 4 + 64 * 32 * ns * 2 * 4 + 256
+    want = 64 * 32 * 128 * 2 + 64 * 32 * ns * 128 * 4 + 64 * 32 * ns * 2 * 4 + 2 * 256
     assert ws(_lib.GQA_OP_DECODE, 64, 32768, 32, 8, 128, _lib.GQA_BF16) == want
     assert ws(_lib.GQA_OP_QK_NORM_ROPE, 4, 4, 4, 4, 128, _lib.GQA_BF16) == 0
     assert ws(_lib.GQA_OP_PREFILL, 1, 8, 6, 4, 128, _lib.GQA_BF16) == 0  # H % G != 0
@@ -256,7 +256,7 @@ def test_decode_split_rule():
     ws = _lib.load().gqa_workspace_bytes
     # the workspace follows the split: 16 splits of 256 keys at max_seq 4096
     assert ws(_lib.GQA_OP_DECODE, 16, 4096, 32, 8, 128, _lib.GQA_BF16) == (
-        16 * 32 * 128 * 2 + 16 * 32 * 16 * 128 * 4 + 16 * 32 * 16 * 2 * 4 + 256)
+        16 * 32 * 128 * 2 + 16 * 32 * 16 * 128 * 4 + 16 * 32 * 16 * 2 * 4 + 2 * 256)
 
 
 def _params(**kw):

@@ -173,3 +173,28 @@ def test_multi_step_graph_equals_eager(per):
     got = to_f64(want_out)
     for s in range(S):
         check(got[s], o_out[s], W.BF16, f"step {s}")
+
+
+def test_multi_step_graph_rejects_bad_shapes():
+    import attention_head_qk_amd as gqa
+    B, H, G, d, S = 2, 8, 2, 128, 64
+    kc = torch.zeros((B, S, G, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    sl = torch.zeros(B, dtype=torch.int32, device="cuda")
+    q = torch.zeros((3, B, H, d), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((3, B, G, d), dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros_like(k)
+    with pytest.raises(ValueError):
+        gqa.DecodeGraph(q, kc, vc, sl, k, v, steps=0)
+    with pytest.raises(ValueError):
+        gqa.DecodeGraph(q, kc, vc, sl, k, v, steps=4)   # q holds 3 steps
+    with pytest.raises(ValueError):
+        gqa.DecodeGraph(q, kc, vc, sl, k[:2], v[:2], steps=3)
+    with pytest.raises(ValueError):
+        gqa.DecodeGraph(q, kc, vc, sl, k, v, steps=3,
+                        positions=torch.zeros((3, B + 1), dtype=torch.int32, device="cuda"))
+    g = gqa.DecodeGraph(q, kc, vc, sl, k, v, steps=3)  # B empty caches: three appends each
+    out = g.launch()
+    g.close()
+    assert out.shape == (3, B, H, d)
+    assert torch.equal(sl, torch.full((B,), 3, dtype=torch.int32, device="cuda"))
