@@ -140,15 +140,16 @@ def test_graph_full_cache_stays_at_max_seq():
     assert not torch.isnan(kc.float()).any()
 
 
-@pytest.mark.parametrize("per", [4, 6])
-def test_multi_step_graph_equals_eager(per):
+@pytest.mark.parametrize("per,dtype,d", [(4, W.BF16, 128), (6, W.BF16, 128), (3, W.F32, 64),
+                                         (2, W.BF16, 64)])
+def test_multi_step_graph_equals_eager(per, dtype, d):
     # gqa_decode_graph_create_steps: `per` steps per launch over [per, B, ...] blocks; two
     # launches (the second with new inputs written between them) equal 2 * per eager steps bit
     # for bit, caches and lengths included
     import attention_head_qk_amd as gqa
     S = 2 * per
-    case = W.make_decode_steps(f"graph_multi{per}", 113 + per, [0, 900, 1023, 2080, 5], S,
-                               2096, H=32, G=8, d=128)
+    case = W.make_decode_steps(f"graph_multi{per}_{dtype}_{d}", 113 + per, [0, 900, 1023, 2080, 5],
+                               S, 2096, H=32, G=8, d=d, dtype=dtype)
     dev = device_steps_inputs(case)
     say("multi-step decode graph", per)
     want_out, want_kc, want_vc, want_sl = _eager_steps(case, dev)
@@ -172,7 +173,7 @@ def test_multi_step_graph_equals_eager(per):
     o_out, _, _ = oracle_decode_steps(case)
     got = to_f64(want_out)
     for s in range(S):
-        check(got[s], o_out[s], W.BF16, f"step {s}")
+        check(got[s], o_out[s], dtype, f"step {s}")
 
 
 def test_multi_step_graph_rejects_bad_shapes():
