@@ -6,8 +6,9 @@
 // cache once and does ~4 FLOP per byte, so it is bound by HBM bandwidth (same section: decode
 // is memory-bound, prefill compute-bound).
 //
-// Split pass. A workgroup takes one split of a.split keys of one sequence and one KV
-// group (and a chunk of HC of the group's h query heads). The K/V cache is token-major
+// Split pass (fp32; the bf16 passes further down run on matrix cores). A workgroup takes one
+// split of a.split keys of one sequence and one KV group (and a chunk of HC of the group's h
+// query heads). The K/V cache is token-major
 // [B, max_seq, G, d], so a key row of one group is d contiguous elements: d/8 lanes read it
 // with 16-byte loads, a wave covers 64/(d/8) rows at once and each row-slot of lanes keeps
 // its own online-softmax state over a batch of 8 keys at a time (8 K and 8 V loads in flight
@@ -243,6 +244,10 @@ __device__ __forceinline__ u32x2_t ds_read_tr16(const char* lds) {
   return __builtin_bit_cast(u32x2_t, v);
 }
 
+// s_waitcnt vmcnt(n), expcnt and lgkmcnt left at their maxima (gfx9 encoding: vmcnt bits
+// [3:0] and [15:14]).
+constexpr int vmcnt_enc(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 // XOR swizzle of the 16-byte chunk index of a staged V row: the four rows one transposing
 // read touches land on four different chunk pairs, so the read is bank-conflict free.
 __device__ __forceinline__ int v_swz(int row) { return 2 * (row & 3); }
@@ -404,10 +409,10 @@ __global__ __launch_bounds__(256, 2) void decode_split_mfma_kernel(DecodeArgs a)
       l_run[ht] += ls;
       pb[ht] = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
     }
-    // ---- this step's V DMA must have landed: only the next step's 16 loads may still be
-    // outstanding (vmcnt(16)), or none at the last step (vmcnt(0))
+    // ---- this step's V DMA must have landed: only the next step's NDMA + 2 KSTEP loads may
+    // still be outstanding, or none at the last step (vmcnt(0))
     if (more) {
-      __builtin_amdgcn_s_waitcnt(0x4F70);
+      __builtin_amdgcn_s_waitcnt(vmcnt_enc(NDMA + 2 * KSTEP));
     } else {
       wait_vmem();
     }
@@ -489,6 +494,262 @@ __global__ __launch_bounds__(256, 2) void decode_split_mfma_kernel(DecodeArgs a)
   }
 }
 
+// ------------------------------------------------------ bf16, whole K rows per load (h <= 16)
+//
+// The split pass for groups of at most 16 query heads with every K load instruction covering
+// whole rows (64 lanes x 16 B = 1024 / 2D rows), as the V DMA does, instead of 64 bytes of each
+// of 16 rows (measured: 64-sequence decode 824 -> 800 us, the 16-sequence loop's pass 21 ->
+// 18 us). Each row (and each query) is cut into NQ = D / 32 interleaved parts: part c holds
+// d = 8 (NQ q + c) + [0, 8) for q = 0..3. In S^T = K Q^T a row of A is one (key, part) pair,
+// m = NQ k + c, so one product covers 16 / NQ keys and the 4 NQ lanes that hold one key read
+// its 2D contiguous bytes; a column of B is one (head, part) pair, n = NQ j + c', for HPM =
+// 16 / NQ heads of the group. Entry (m, n) is then the dot product of part c of key k with
+// part c' of head j: the entries with c = c' are partial scores, summed over the NQ adjacent
+// lanes of a head by DPP, and the others are dropped. Groups of more than HPM heads take NHQ
+// such products per 32 keys, one per set of HPM heads; column n = NQ j + c' then follows head
+// (c' mod NHQ) HPM + j from the scores on, so the softmax, P^T and O^T columns cover every
+// head once or more. The rest is the kernel above: V by DMA with transposing reads, the lazy
+// softmax reference, two steps in flight per wave, and the 4 waves' states merged through LDS.
+namespace {
+
+// XOR swizzle of the 16-byte chunk index of a staged V row for the key order of this kernel:
+// the four rows one 16-lane block of a transposing read addresses differ in bits 2-3 of the
+// row (d = 128) or in bits 0 and 3 (d = 64), and land on four different chunk pairs.
+template <int D>
+__device__ __forceinline__ int v_swz_rows(int row) {
+  return D == 128 ? 2 * ((row >> 2) & 3) : 2 * ((row & 1) | ((row >> 2) & 2));
+}
+
+}  // namespace
+
+template <int D, int NHQ, bool NTV>
+__global__ __launch_bounds__(256, 2) void decode_split_rows_kernel(DecodeArgs a) {
+  constexpr int NQ = D / 32;       // parts of a row
+  constexpr int KPM = 16 / NQ;     // keys per S^T product
+  constexpr int HPM = 16 / NQ;     // heads per S^T product
+  constexpr int KQ = 4 / NQ;       // keys per lane per S^T product
+  constexpr int NMF = 32 / KPM;    // S^T products per 32-key step
+  constexpr int NMT = D / 16;      // 16-row tiles of O^T
+  constexpr int SUB = 32;          // keys per step of a wave
+  constexpr int ROWB = D * 2;      // bytes of one row
+  constexpr int SUBB = SUB * ROWB; // one staged V sub-tile
+  constexpr int NDMA = SUBB / 1024;
+  constexpr int DCH = D / 8;
+  constexpr int NLOAD = NDMA + NMF;  // vector-memory instructions per step
+  static_assert(4 * 16 * D * 4 <= 4 * SUBB, "merge scratch fits a V buffer");
+  static_assert(NHQ >= 1 && NHQ * HPM <= 16 && NHQ <= NQ, "at most 16 heads, each in a column");
+  __shared__ __attribute__((aligned(16))) char vb0[4 * SUBB];
+  __shared__ __attribute__((aligned(16))) char vb1[4 * SUBB];
+  __shared__ float sm_ml[2][4][16];
+
+  // grid: x = group, y = split, z = sequence (as above)
+  const int g = blockIdx.x;
+  const int s = blockIdx.y;
+  const int b = blockIdx.z;
+  const int L = a.seq_lens[b];
+  const int k0 = s * a.split;
+  if (k0 >= L) return;
+  const int k1 = (k0 + a.split < L) ? k0 + a.split : L;
+  const int kpw = a.split / 4;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, q4 = lane >> 4;
+  const int part = l16 % NQ;  // the part of its key (A) or head (B) this lane holds
+  const int hd = l16 / NQ;    // its key inside a product (A), its head inside a set (B)
+  const int jq = part % NHQ;  // the head set of this lane's column from the scores on
+  const int head = jq * HPM + hd;  // and its head
+  const int h = a.h;
+  const float sl2e = a.scale_log2e;
+
+  // ---- Q^T (B operands, one per head set): column l16 = (head t HPM + hd, part)
+  bf16x8_t qf[NHQ];
+  {
+    const bf16_t* qt = reinterpret_cast<const bf16_t*>(a.qt) + ((long)b * a.H + (long)g * h) * D;
+#pragma unroll
+    for (int t = 0; t < NHQ; ++t) {
+      const int hh = t * HPM + hd;
+      u32x4_t w = {0u, 0u, 0u, 0u};
+      if (hh < h) w = *reinterpret_cast<const u32x4_t*>(qt + (long)hh * D + 8 * (NQ * q4 + part));
+      qf[t] = as_bf16x8(w);
+    }
+  }
+
+  // ---- buffer descriptors over sequence b's rows of group g; rows >= L read as zero
+  const int row_stride = a.G * D * 2;
+  const long base_el = ((long)b * a.max_seq * a.G + g) * D;
+  const int nrec = (L - 1) * row_stride + D * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(reinterpret_cast<const bf16_t*>(a.k_cache) + base_el, nrec);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(reinterpret_cast<const bf16_t*>(a.v_cache) + base_el, nrec);
+
+  f32x4_t o[NMT];
+  float m_run = -INFINITY, l_run = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt) o[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  char* const vbw[2] = {vb0 + wave * SUBB, vb1 + wave * SUBB};
+  const int kw0 = k0 + wave * kpw;
+  const int kw1 = (kw0 + kpw < k1) ? kw0 + kpw : k1;
+  const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+
+  // key (inside a step) of probability slot e of this lane: product e / KQ, its key
+  // KQ q4 + e % KQ
+  auto key_of = [&](int e) { return KPM * (e / KQ) + KQ * q4 + e % KQ; };
+
+  // Loads of one 32-key step: V rows by DMA (as above, with this kernel's swizzle) and, for
+  // product mi, K row kb + KPM mi + hd, part `part` into A-operand registers.
+  u32x4_t kr[2][NMF];
+  auto issue = [&](int kb, int buf, u32x4_t (&k)[NMF]) {
+#pragma unroll
+    for (int n = 0; n < NDMA; ++n) {
+      const int r = n * (1024 / ROWB) + lane / DCH;
+      const int c = (lane % DCH) ^ v_swz_rows<D>(r);
+      dma16<NTV ? kNonTemporal : 0>(vrs, vbw[buf] + n * 1024, (kb + r) * row_stride + c * 16, 0);
+    }
+#pragma unroll
+    for (int mi = 0; mi < NMF; ++mi)
+      k[mi] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+          krs, (kb + KPM * mi + hd) * row_stride + (NQ * q4 + part) * 16, 0, 0));
+  };
+
+  auto step = [&](int kb, int buf, const u32x4_t (&k)[NMF], bool more) {
+    // ---- scores of keys kb + key_of(e), e = 0..7, for this lane's head (the same in the
+    // lanes of its column across q4). In a product's result lane (q4, n) slot i is row
+    // 4 q4 + i: key KQ q4 + i / NQ, part i % NQ; the slots of the lane's own part are the
+    // partial scores of head t HPM + hd.
+    float sc[8];
+#pragma unroll
+    for (int t = 0; t < NHQ; ++t)
+#pragma unroll
+      for (int mi = 0; mi < NMF; ++mi) {
+        const f32x4_t acc = mfma16(as_bf16x8(k[mi]), qf[t], f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int u = 0; u < KQ; ++u) {
+          float v = acc[NQ * u];
+#pragma unroll
+          for (int c = 1; c < NQ; ++c) v = part == c ? acc[NQ * u + c] : v;
+          v = dpp_add<0xB1>(v);                 // + part c ^ 1
+          if (NQ == 4) v = dpp_add<0x4E>(v);    // + parts c ^ 2, c ^ 3
+          sc[KQ * mi + u] = (t == 0 || jq == t) ? v : sc[KQ * mi + u];
+        }
+      }
+    if (kb + SUB > kw1) {  // the last step of the sequence: keys >= kw1 are not there
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (kb + key_of(e) >= kw1) sc[e] = -INFINITY;
+    }
+    // ---- probabilities (P^T as the B operand: slot e is key key_of(e))
+    uint32_t pk[4];
+    float ls;
+    auto probs = [&]() {
+      ls = 0.f;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        f32x2_t pp = {__builtin_amdgcn_exp2f(fmaf(sc[2 * p], sl2e, -m_run)),
+                      __builtin_amdgcn_exp2f(fmaf(sc[2 * p + 1], sl2e, -m_run))};
+        const bf16x2_t pb2 = __builtin_convertvector(pp, bf16x2_t);
+        pk[p] = __builtin_bit_cast(uint32_t, pb2);
+        ls = __builtin_amdgcn_fdot2_f32_bf16(pb2, one2, ls, false);
+      }
+    };
+    probs();
+    if (__any(!(ls <= 0x1p32f))) {
+      float mx = sc[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+      mx = fmaxf(mx, xor_shfl(mx, 16));
+      mx = fmaxf(mx, xor_shfl(mx, 32)) * sl2e;
+      const float m_new = fmaxf(m_run, mx);
+      if (m_new != -INFINITY) {  // padded or fully masked heads keep their state
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt) o[mt] *= alpha;
+        m_run = m_new;
+      }
+      probs();
+    }
+    l_run += ls;
+    const bf16x8_t pb = as_bf16x8(u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+    // ---- this step's V DMA must have landed: only the next step's loads may be outstanding
+    if (more) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_enc(NLOAD));
+    } else {
+      wait_vmem();
+    }
+    // ---- O^T += V^T P^T; V^T operand: lane (d = 16 mt + l16) gets the keys of slots 0-3 from
+    // the first transposing read and of slots 4-7 from the second (addressing lane 4j + r of a
+    // 16-lane block supplies slot j (+4), d = 16 mt + 4 r + [0, 4))
+    const char* vbuf = vbw[buf];
+    const int r0 = key_of(l16 >> 2), r1 = key_of((l16 >> 2) + 4);
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) {
+      const int c = 2 * mt + ((l16 & 3) >> 1);
+      const int off8 = (l16 & 1) * 8;
+      const u32x2_t v0 = ds_read_tr16(vbuf + r0 * ROWB + ((c ^ v_swz_rows<D>(r0)) * 16) + off8);
+      const u32x2_t v1 = ds_read_tr16(vbuf + r1 * ROWB + ((c ^ v_swz_rows<D>(r1)) * 16) + off8);
+      const bf16x8_t va = as_bf16x8(u32x4_t{v0[0], v0[1], v1[0], v1[1]});
+      o[mt] = mfma16(va, pb, o[mt]);
+    }
+  };
+
+  const int nsteps = (kw1 - kw0 + SUB - 1) / SUB;
+  if (nsteps > 0) issue(kw0, 0, kr[0]);
+  int u = 0;
+  for (; u + 2 < nsteps; u += 2) {
+    issue(kw0 + (u + 1) * SUB, 1, kr[1]);
+    step(kw0 + u * SUB, 0, kr[0], true);
+    issue(kw0 + (u + 2) * SUB, 0, kr[0]);
+    step(kw0 + (u + 1) * SUB, 1, kr[1], true);
+  }
+  if (u + 1 < nsteps) {
+    issue(kw0 + (u + 1) * SUB, 1, kr[1]);
+    step(kw0 + u * SUB, 0, kr[0], true);
+    step(kw0 + (u + 1) * SUB, 1, kr[1], false);
+  } else if (u < nsteps) {
+    step(kw0 + u * SUB, 0, kr[0], false);
+  }
+
+  // ---- merge the 4 waves' states: (m, l) per head and the O columns as [w][head][D] floats
+  // in V buffer 0, from the first column of each head (part < NHQ)
+  __syncthreads();
+  {
+    float lt = l_run + xor_shfl(l_run, 16);
+    lt += xor_shfl(lt, 32);
+    if (q4 == 0 && part < NHQ) {
+      sm_ml[0][wave][head] = m_run;
+      sm_ml[1][wave][head] = lt;
+    }
+    float* sm_o = reinterpret_cast<float*>(vb0);
+    if (part < NHQ)
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm_o[(wave * 16 + head) * D + 16 * mt + 4 * q4 + i] = o[mt][i];
+  }
+  __syncthreads();
+  const float* sm_o = reinterpret_cast<const float*>(vb0);
+  for (int idx = tid; idx < h * D; idx += 256) {
+    const int hh = idx / D, d = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_ml[0][w][hh]);
+    float Ls = 0.f, Os = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float wt = __builtin_amdgcn_exp2f(sm_ml[0][w][hh] - M);  // empty waves: 0
+      Ls = fmaf(sm_ml[1][w][hh], wt, Ls);
+      Os = fmaf(sm_o[(w * 16 + hh) * D + d], wt, Os);
+    }
+    const long pidx = ((long)b * a.H + (long)g * h + hh) * a.nsplit + s;
+    a.part_o[pidx * D + d] = Os;
+    if (d == 0) {
+      a.part_ml[2 * pidx] = M;
+      a.part_ml[2 * pidx + 1] = Ls;
+    }
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
   __shared__ float sw[kMaxCombineSplits];
@@ -527,8 +788,27 @@ static hipError_t launch_split_mfma(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, int NHQ>
+static hipError_t launch_split_rows(const DecodeArgs& a, hipStream_t s) {
+  const dim3 grid(a.G, a.nsplit, a.B);
+  if (a.stream_v)
+    hipLaunchKernelGGL((decode_split_rows_kernel<D, NHQ, true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_split_rows_kernel<D, NHQ, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// Whole-row K loads with NHQ sets of 16 / (D / 32) heads for h <= 16. Four sets (d = 128,
+// h > 8) take four times the score products of the tiled kernel, which only pays where the
+// pass streams a large cache (measured: 64 sequences of up to 32768 keys 491 -> 476 us; 16
+// sequences of about 1200 keys 13.8 -> 15.1 us); otherwise, and for h > 16, the tiled kernel.
 template <int D>
 static hipError_t split_mfma_d(const DecodeArgs& a, hipStream_t s) {
+  constexpr int HPM = 16 / (D / 32);
+  if (a.h <= HPM) return launch_split_rows<D, 1>(a, s);
+  if (a.h <= 2 * HPM) return launch_split_rows<D, 2>(a, s);
+  if constexpr (D == 128)
+    if (a.h <= 16 && a.stream_v) return launch_split_rows<D, 4>(a, s);
   return a.h <= 16 ? launch_split_mfma<D, 1>(a, s) : launch_split_mfma<D, 2>(a, s);
 }
 

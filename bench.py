@@ -206,7 +206,7 @@ class PrefillCached:
 
 
 class Decode:
-    kernel = "decode_split_mfma_kernel"
+    kernel = "decode_split_rows_kernel"
 
     def __init__(self, case):
         import torch
@@ -671,8 +671,8 @@ def bench_decode_loop(args, dev_name):
             "roofline": {"bound": "hbm", "achieved": round(gbs(kern_ms), 2),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs(kern_ms) / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic("decode_split_mfma_kernel", c.name),
-                         "kernel": "decode_split_mfma_kernel", "kernel_ms": round(kern_ms, 5)},
+                         "traffic": measured_traffic("decode_split_rows_kernel", c.name),
+                         "kernel": "decode_split_rows_kernel", "kernel_ms": round(kern_ms, 5)},
             "config": {"workload": c.name, "B": c.B, "steps_per_block": c.S,
                        "cache_lens": c.cache_lens.tolist(), "max_seq": c.max_seq, "H": c.H,
                        "G": c.G, "d": c.d, "seed": c.seed},
