@@ -116,3 +116,39 @@ def test_decode_deterministic():
     a = run_decode(case, dev)
     b = run_decode(case, dev)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_decode_independent_of_split_length(dtype):
+    # The same four sequences in caches of 4096 and 32768 rows, and among 60 empty ones: the
+    # host picks 256-, 512- and 1024-key splits. The cross-split merge regroups the softmax
+    # exactly (D1-2), so the three results differ only by rounding: in fp32 by a few ulps; in
+    # bf16 also through the probabilities' rounding to bf16 against a running reference that
+    # depends on where the splits fall.
+    import dataclasses
+    import attention_head_qk_amd as gqa
+    lens = [4000, 1, 2049, 777]
+    base = W.make_decode("splitinv", 97, B=4, max_seq=4096, H=32, G=8, d=128, dtype=dtype,
+                         seq_lens=lens)
+
+    def padded(B, max_seq):
+        pad = lambda x: np.concatenate([x, np.zeros((B - 4,) + x.shape[1:], x.dtype)])
+        return dataclasses.replace(base, max_seq=max_seq, q=pad(base.q), k_new=pad(base.k_new),
+                                   v_new=pad(base.v_new),
+                                   seq_lens=np.array(lens + [0] * (B - 4), dtype=np.int32))
+
+    outs, splits = [], []
+    for B, max_seq in [(4, 4096), (4, 32768), (64, 32768)]:
+        case = padded(B, max_seq)
+        splits.append(gqa.decode_split_keys(B, case.H, case.G, max_seq))
+        say("decode split invariance", dtype, "B", B, "max_seq", max_seq, "split", splits[-1])
+        outs.append(to_f64(run_decode(case, device_decode_inputs(case)))[:4])
+    assert sorted(splits) == [256, 512, 1024], splits
+    for b in range(4):
+        want, _, _ = oracle_decode_seq(base, b)
+        check(outs[0][b], want, dtype, f"b={b}")
+    for o in outs[1:]:
+        if dtype == W.F32:
+            assert np.abs(o - outs[0]).max() <= 2e-6
+        else:
+            assert np.all(np.abs(o - outs[0]) <= 2.0 ** -6 * np.abs(outs[0]) + 2.0 ** -9)
