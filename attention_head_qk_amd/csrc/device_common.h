@@ -155,6 +155,8 @@ struct PrologueArgs {
   int32_t* lens_out;  // decode, generation-loop step: non-null = the sequence gains its new
                       // token here (length min(seq_lens[b] + 1, max_seq)), and that length is
                       // written to lens_out[b] for the rest of the step
+  int32_t* zero;      // prefill: zero_n counters the attention kernel that follows claims
+  int zero_n;         // its blocks from (zeroed by the first workgroup), or null
   double omega[kMaxHalfD];  // theta^(-2j/d), computed on the host in fp64
 };
 
@@ -174,6 +176,8 @@ struct PrefillArgs {
   int n_blk;          // column blocks of the longest sequence
   int zigzag;         // 1: pair heavy and light blocks (see the prefill kernel)
   int rank_chunk;     // bf16 kernel: consecutive ranks of one sequence before the next one
+  int32_t* claim;     // bf16 kernel: [G] zeroed counters; non-null = a workgroup takes its
+                      // rank inside its group from claim[g] instead of from its block id
   const int32_t* cache_lens;  // bf16 kernel, cached prefill: earlier tokens per sequence in
                               // the cache; kt / v are then caches [B, max_seq, G, D]
   int max_seq;

@@ -43,7 +43,9 @@
 //   fastest-varying part of the block id, which keeps the blocks of one KV group on the same
 //   XCD (blocks are dealt round-robin over the 8 XCDs) when G is a multiple of 8, so its K/V
 //   stay in that XCD's L2; with several sequences the ranks go in runs of 32 per sequence, so
-//   an XCD streams few sequences' K/V at a time.
+//   an XCD streams few sequences' K/V at a time. When a group spans several XCDs (G < 8) the
+//   unmasked kernel's workgroups claim their ranks from a counter per group, so faster XCDs
+//   take more of the work.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -122,9 +124,20 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   // complementary causal work (n_blk - r and r + 1 tiles).
   // With rank_chunk > 1 the ranks go in chunks: the B sequences take turns with runs of
   // rank_chunk consecutive ranks each, so an XCD holds the K/V of fewer sequences at once.
+  // With a.claim the rank inside the group is taken from a counter instead of the block id:
+  // the dispatcher hands every XCD the same number of workgroups, and under load the XCDs
+  // run at different clocks, so a fixed share of blocks per XCD ends with the slowest one;
+  // claimed in time order, the heaviest-first ranks go to whichever workgroups start first.
   const int id = blockIdx.x;
   const int g = id % a.G;
-  const int rest = id / a.G;
+  int rest = id / a.G;
+  if constexpr (MASK == 0 && !CACHE) if (a.claim) {
+    __shared__ int s_rank;
+    if (tid == 0)
+      s_rank = __hip_atomic_fetch_add(a.claim + g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    rest = __builtin_amdgcn_readfirstlane(s_rank);
+  }
   int b, r;
   if (a.rank_chunk > 1) {
     const int chunk = rest / (a.B * a.rank_chunk);

@@ -227,10 +227,10 @@ def test_workspace_bytes():
     lib = _lib.load()
     ws = lib.gqa_workspace_bytes
     # prefill: k~ [N,G,d] in the element type (fp32 also q~ [N,H,d]), each rounded up to
-    # 256 bytes; the bf16 attention kernel prepares Q itself
-    assert ws(_lib.GQA_OP_PREFILL, 1, 4096, 16, 8, 128, _lib.GQA_BF16) == 4096 * 8 * 128 * 2
+    # 256 bytes; the bf16 attention kernel prepares Q itself and has G block counters
+    assert ws(_lib.GQA_OP_PREFILL, 1, 4096, 16, 8, 128, _lib.GQA_BF16) == 4096 * 8 * 128 * 2 + 256
     assert ws(_lib.GQA_OP_PREFILL, 1, 3, 2, 1, 64, _lib.GQA_F32) == 1536 + 768
-    assert ws(_lib.GQA_OP_PREFILL, 1, 3, 1, 1, 64, _lib.GQA_BF16) == 512  # 384 -> 512
+    assert ws(_lib.GQA_OP_PREFILL, 1, 3, 1, 1, 64, _lib.GQA_BF16) == 512 + 256  # 384 -> 512
     # decode: q~ + fp32 partial O + fp32 (m, l) per split + two [B] step-length buffers
     S = lib.gqa_decode_split_keys(64, 32, 8, 32768)
     assert S == 1024
