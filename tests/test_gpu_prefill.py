@@ -53,6 +53,19 @@ def test_long_32k_sampled_rows(G):
     say(case.name, len(rows), "rows", stats)
 
 
+@pytest.mark.parametrize("T,H,G", [(8192, 32, 2), (6000, 48, 3)])
+def test_claimed_ranks_sampled_rows(T, H, G):
+    # grids of more than two rounds whose groups each span several XCDs (G < 8): the
+    # workgroups take their ranks from the per-group counters instead of their block ids
+    import _oracle_pool as OP
+    case = W.make_prefill(f"claims_T{T}_H{H}_G{G}", 131 + G, lengths=[T], H=H, G=G, d=128)
+    say("prefill with claimed ranks", T, H, G)
+    got = to_f64(run_prefill(case))
+    rows = OP.sample_rows(case, 256, seed=G)
+    stats = check(got[rows], oracle_prefill_rows(case, rows), W.BF16, case.name)
+    say(case.name, len(rows), "rows", stats)
+
+
 SHAPES = [
     # (lengths, H, G, d, causal)
     ([1], 4, 2, 128, True),
