@@ -39,12 +39,12 @@ def edge_lens(S):
 @pytest.mark.parametrize("dtype", [W.BF16, W.F32])
 @pytest.mark.parametrize("H,G,d", [(32, 8, 128), (12, 4, 128), (8, 8, 64), (16, 1, 128),
                                    (6, 2, 64), (40, 1, 128), (64, 8, 128), (10, 2, 128),
-                                   (16, 1, 64), (24, 2, 64), (64, 4, 128)])
+                                   (16, 1, 64), (24, 2, 64), (64, 4, 128), (8, 8, 128)])
 def test_decode_edge_lengths(dtype, H, G, d, max_seq):
     # the split length follows the shape (1024, 512 and 256 all occur over these cases); the
     # lengths sit on that split's edges. At max_seq 24576 the bf16 caches of the G = 8 and
     # G = 4 shapes exceed 512 MiB, so those cases take the pass that streams V non-temporally.
-    # Group sizes: h = 1..4 (one head set of the whole-row pass at d = 128), 5..8 (two sets),
+    # Group sizes: h = 1, 3 and 4 (one head set of the whole-row pass at d = 128), 5..8 (two sets),
     # 16 at G = 4 (four sets when streamed, else the tiled pass), 16 at G = 1 (tiled), 40
     # (tiles of 32 heads); at d = 64: 1, 3 (one set), 12 and 16 (two sets).
     import attention_head_qk_amd as gqa
