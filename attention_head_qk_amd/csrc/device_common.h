@@ -178,6 +178,10 @@ struct PrefillArgs {
   int rank_chunk;     // bf16 kernel: consecutive ranks of one sequence before the next one
   int32_t* claim;     // bf16 kernel: [G] zeroed counters; non-null = a workgroup takes its
                       // rank inside its group from claim[g] instead of from its block id
+  float* pair_part;   // bf16 kernel, paired schedule of a one-round grid (non-null): per pair
+                      // two partial softmax states of COLS columns (O [COLS][D], then (m, l)
+                      // per column), and a zeroed arrival counter per pair
+  int32_t* pair_arrive;
   const int32_t* cache_lens;  // bf16 kernel, cached prefill: earlier tokens per sequence in
                               // the cache; kt / v are then caches [B, max_seq, G, D]
   int max_seq;

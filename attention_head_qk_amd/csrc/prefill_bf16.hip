@@ -81,7 +81,7 @@ __device__ __forceinline__ u32x2_t ds_read_tr16(const char* lds) {
 
 // MASK: bit 0 = sliding window (a.window), bit 1 = 64-key block layout (a.block_mask).
 // CACHE: keys come from caches after a.cache_lens[b] earlier rows (cached prefill).
-template <int D, int MASK, bool CACHE>
+template <int D, int MASK, bool CACHE, bool PAIR>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int DCH = D / 8;               // 16-byte chunks per K row
   constexpr int NST = D / 16;              // k-steps of S^T = K Q^T
@@ -151,6 +151,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   }
   const int half_r = (a.n_blk + 1) / 2;
   const int blk = (a.zigzag && r >= half_r) ? r - half_r : a.n_blk - 1 - r;
+
+  // ---- one column block `blk` of sequence b, key tiles [t_lo, min(t_hi, its tiles)): with
+  // slot < 0 the block's output; otherwise (paired schedule) this part's softmax state goes
+  // to partial slot `slot` (0: the heavy block's own part, 1: the part its light partner
+  // took), and the part that ends last merges the two and writes the output
+  __shared__ int s_arrived;
+  auto run = [&](const int blk, const int t_lo, const int t_hi, const int pair, const int slot) {
   int seq0, Tb;
   if (a.cu_seqlens) {
     seq0 = a.cu_seqlens[b];
@@ -606,9 +613,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   // compiler groups the MFMAs ahead of the exponentials. Four accumulator chains for S^T
   // here measured no better than two.)
   constexpr int PPR = 16 / NST;  // probability pairs per lane per S round
+  const int t_end = t_hi < ntiles ? t_hi : ntiles;
   auto pstep = [&](int P, int t, f32x16_t (&sc)[2]) {
-    const int tk = t + 2 < ntiles ? t + 2 : ntiles - 1;
-    const int tv = t + 1 < ntiles ? t + 1 : ntiles - 1;
+    const int tk = t + 2 < t_end ? t + 2 : t_end - 1;
+    const int tv = t + 1 < t_end ? t + 1 : t_end - 1;
     issue_k(P, tk);      // K(t+2) -> kbuf P (K(t) was consumed by the previous step)
     issue_v(1 - P, tv);  // V(t+1) -> vbuf 1-P
     mask_tile(sc, t);
@@ -658,9 +666,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   };
 
   if constexpr (MASK == 0) {
-    issue_k(0, 0);
-    issue_v(0, 0);
-    issue_k(1, ntiles > 1 ? 1 : 0);
+    issue_k(0, t_lo);
+    issue_v(0, t_lo);
+    issue_k(1, t_lo + 1 < t_end ? t_lo + 1 : t_lo);
     fill_omega();
     if (rope_tab) {
       build_rope_table();
@@ -670,14 +678,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
     wait_vmem();
     __syncthreads();
     f32x16_t sc[2];
-    s_product(0, sc);  // S^T of tile 0
+    s_product(0, sc);  // S^T of tile t_lo
     __syncthreads();   // kbuf 0 is refilled by the first step
-    int t = 0;
-    for (; t + 1 < ntiles; t += 2) {
+    int t = t_lo;
+    for (; t + 1 < t_end; t += 2) {
       pstep(0, t, sc);
       pstep(1, t + 1, sc);
     }
-    if (t < ntiles) pstep(0, t, sc);
+    if (t < t_end) pstep(0, t, sc);
   } else {
     // visible tiles only; past the last one the loads repeat it (same instruction stream)
     int t = (MASK & 2) ? next_tile(t_first - 1) : t_first;
@@ -703,7 +711,63 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
   }
 
   // ---- epilogue: O / l -> bf16
-  const float l_tot = l_run + xor_shfl(l_run, 32);
+  float l_tot = l_run + xor_shfl(l_run, 32);
+  if constexpr (PAIR) {
+    if (slot >= 0) {
+      // Paired schedule: store this part's state (this lane's O rows, then the column's
+      // reference m and sum l) with device-coherent 16-byte stores (the partner may run on
+      // another XCD), laid out so that each store instruction of a wave writes 1 KB in one
+      // piece; then count the part in. The part counted second reads the other one back and
+      // merges, the heavy block's own part always as the first operand, so the bits do not
+      // depend on which part ends last.
+      constexpr int PF = COLS * D + 2 * COLS;  // floats of one part
+      constexpr int kCoherent = 16;            // cache policy: sc1 (device-coherent access)
+      const __amdgpu_buffer_rsrc_t prs = make_rsrc(a.pair_part + (long)pair * 2 * PF, 2 * PF * 4);
+      const int mine = slot * PF * 4, other = (1 - slot) * PF * 4;  // byte offsets of the parts
+      const int cw = wave * 32 + l32;  // column inside the block
+      auto o_off = [&](int mt, int r4) { return ((((mt * 4 + r4) * 2 + grp) * COLS + cw) * 4) * 4; };
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4_t v = {o[mt][4 * r4], o[mt][4 * r4 + 1], o[mt][4 * r4 + 2], o[mt][4 * r4 + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), prs, mine + o_off(mt, r4), 0,
+                                                 kCoherent);
+        }
+      if (grp == 0) {
+        const f32x2_t ml = {m_run, l_tot};
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, ml), prs,
+                                              mine + (COLS * D + 2 * cw) * 4, 0, kCoherent);
+      }
+      wait_vmem();
+      __syncthreads();
+      if (tid == 0)
+        s_arrived = __hip_atomic_fetch_add(a.pair_arrive + pair, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (__builtin_amdgcn_readfirstlane(s_arrived) == 0) return;  // the other part merges
+      const f32x2_t mlo = __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
+          prs, other + (COLS * D + 2 * cw) * 4, 0, kCoherent));
+      const float mA = slot == 0 ? m_run : mlo[0], mB = slot == 0 ? mlo[0] : m_run;
+      const float lA = slot == 0 ? l_tot : mlo[1], lB = slot == 0 ? mlo[1] : l_tot;
+      const float M = fmaxf(mA, mB);
+      const float wA = __builtin_amdgcn_exp2f(mA - M), wB = __builtin_amdgcn_exp2f(mB - M);
+      l_tot = fmaf(lB, wB, lA * wA);
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt) {
+        f32x4_t ot[4];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          ot[r4] = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+              prs, other + o_off(mt, r4), 0, kCoherent));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float oth = ot[i >> 2][i & 3];
+          const float oA = slot == 0 ? o[mt][i] : oth, oB = slot == 0 ? oth : o[mt][i];
+          o[mt][i] = fmaf(oB, wB, oA * wA);
+        }
+      }
+    }
+  }
   const float inv = 1.0f / l_tot;
   if (cvalid) {
     bf16_t* op = reinterpret_cast<bf16_t*>(a.out) + ((long)(seq0 + pcol) * a.H + head) * D;
@@ -718,12 +782,56 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
       }
     }
   }
+  };  // run
+
+  if constexpr (PAIR) {
+    // Paired schedule of a one-round dense causal grid: heavy block n_blk - 1 - rh and light
+    // block rh of the same (sequence, group) run side by side (block ids i and i + grid/2).
+    // The heavy one alone would run most of its tiles without a partner on its CU, so its key
+    // tiles are cut at a fixed point s: the heavy workgroup takes [0, s), the light one first
+    // takes [s, n_h) of the heavy block and then its own block. s follows from the two tile
+    // counts alone (the light workgroup runs at about 0.7 of the heavy one's rate beside it,
+    // plus its second start), so both workgroups derive the same cut and the result does not
+    // depend on timing: s = ceil(0.55 (n_h + n_l + 2)), the best of 0.5-0.7 measured.
+    auto tiles_of = [&](int bk) {
+      const int nc = a.T * a.h, c0 = bk * COLS;
+      if (c0 >= nc) return 0;
+      const int cmax = (c0 + COLS - 1 < nc) ? c0 + COLS - 1 : nc - 1;
+      return ((int)((unsigned)cmax / (unsigned)a.h) + 1 + KT - 1) / KT;
+    };
+    const bool heavy = r < half_r;
+    const int rh = heavy ? r : r - half_r;  // the pair's heavy rank; its light block is rh
+    const int n_h = tiles_of(a.n_blk - 1 - rh);
+    const int n_l = rh + half_r < a.n_blk ? tiles_of(rh) : 0;
+    const int cut = n_l > 0 ? min(n_h, (11 * (n_h + n_l + 2) + 19) / 20) : n_h;
+    const int pair = (rh * a.B + b) * a.G + g;
+    // one copy of the block code: the light workgroup runs it twice (the heavy block's tiles
+    // it takes, then its own block)
+    const int nphase = (!heavy && cut < n_h) ? 2 : 1;
+    for (int ph = 0; ph < nphase; ++ph) {
+      const bool own_light = !heavy && ph == nphase - 1;
+      const int bk = own_light ? rh : a.n_blk - 1 - rh;
+      const int lo = (!heavy && !own_light) ? cut : 0;
+      const int hi = heavy ? cut : 0x7fffffff;
+      const int sl = own_light ? -1 : (heavy ? (cut < n_h ? 0 : -1) : 1);
+      run(bk, lo, hi, pair, sl);
+    }
+  } else {
+    run(blk, 0, 0x7fffffff, -1, -1);
+  }
 }
 
 template <int D, int MASK, bool CACHE>
 static hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
   const long grid = (long)a.B * a.G * a.n_blk;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, MASK, CACHE>), dim3((unsigned)grid), dim3(256), 0,
+  if constexpr (MASK == 0 && !CACHE) {
+    if (a.pair_part) {
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, 0, false, true>), dim3((unsigned)grid), dim3(256),
+                         0, s, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, MASK, CACHE, false>), dim3((unsigned)grid), dim3(256), 0,
                      s, a);
   return hipGetLastError();
 }

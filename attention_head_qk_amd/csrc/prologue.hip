@@ -158,7 +158,8 @@ __device__ __forceinline__ void prologue_block(const PrologueArgs& a, unsigned b
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void qk_norm_rope_kernel(PrologueArgs a) {
-  if (a.zero && blockIdx.x == 0 && threadIdx.x < (unsigned)a.zero_n) a.zero[threadIdx.x] = 0;
+  if (a.zero && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < a.zero_n; i += 256) a.zero[i] = 0;
   prologue_block<T, D>(a, blockIdx.x, threadIdx.x);
 }
 

@@ -115,7 +115,7 @@ int main(void) {
 
   /* sizes and rules */
   EXPECT(gqa_workspace_bytes(GQA_OP_PREFILL, 1, 4096, 16, 8, 128, GQA_BF16) ==
-         (size_t)4096 * 8 * 128 * 2 + 256);
+         (size_t)4096 * 8 * 128 * 2 + 1280 + (size_t)256 * 2 * (128 * 128 + 256) * 4);
   EXPECT(gqa_workspace_bytes(GQA_OP_PREFILL, 1, 8, 6, 4, 128, GQA_BF16) == 0);
   EXPECT(gqa_workspace_bytes(99, 1, 8, 8, 8, 128, GQA_BF16) == 0);
   EXPECT(gqa_decode_split_keys(64, 32, 8, 32768) == 1024);

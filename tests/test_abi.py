@@ -227,10 +227,18 @@ def test_workspace_bytes():
     lib = _lib.load()
     ws = lib.gqa_workspace_bytes
     # prefill: k~ [N,G,d] in the element type (fp32 also q~ [N,H,d]), each rounded up to
-    # 256 bytes; the bf16 attention kernel prepares Q itself and has G block counters
-    assert ws(_lib.GQA_OP_PREFILL, 1, 4096, 16, 8, 128, _lib.GQA_BF16) == 4096 * 8 * 128 * 2 + 256
+    # 256 bytes; the bf16 attention kernel prepares Q itself and has G block counters, and
+    # grids of at most 512 workgroups (B G ceil(T h / 128)) may run the paired schedule: one
+    # counter and two fp32 partial states (128 columns x (d + 2)) per pair of column blocks
+    def part(pairs, d):
+        return pairs * 2 * (128 * d + 256) * 4
+    pairs = 8 * 32                                       # T=4096, h=2: 64 blocks per group
+    assert ws(_lib.GQA_OP_PREFILL, 1, 4096, 16, 8, 128, _lib.GQA_BF16) == (
+        4096 * 8 * 128 * 2 + 1280 + part(pairs, 128))    # (8 + 256) counters -> 1280 bytes
     assert ws(_lib.GQA_OP_PREFILL, 1, 3, 2, 1, 64, _lib.GQA_F32) == 1536 + 768
-    assert ws(_lib.GQA_OP_PREFILL, 1, 3, 1, 1, 64, _lib.GQA_BF16) == 512 + 256  # 384 -> 512
+    assert ws(_lib.GQA_OP_PREFILL, 1, 3, 1, 1, 64, _lib.GQA_BF16) == 512 + 256 + part(1, 64)
+    # a grid of more than 512 workgroups (T=32768, h=16: 4096 blocks x 4 groups): no pairs
+    assert ws(_lib.GQA_OP_PREFILL, 1, 32768, 64, 4, 128, _lib.GQA_BF16) == 32768 * 4 * 256 + 256
     # decode: q~ + fp32 partial O + fp32 (m, l) per split + two [B] step-length buffers
     S = lib.gqa_decode_split_keys(64, 32, 8, 32768)
     assert S == 1024

@@ -217,6 +217,20 @@ def test_default_positions_and_k_out():
     assert np.all(err <= 2.0 ** -8 * np.abs(kt) + 1e-6)
 
 
+@pytest.mark.parametrize("T,H,G", [(4096, 16, 8), (3100, 24, 8), (4000, 8, 2)])
+def test_paired_schedule(T, H, G):
+    # one-round grids whose heavy blocks share their key tiles with their light partners
+    # (fixed cut, partial states merged by whichever part ends last): every element against
+    # the oracle, and bit-identical on a second run
+    case = W.make_prefill(f"paired_T{T}_H{H}_G{G}", 141 + H + G, lengths=[T], H=H, G=G, d=128)
+    dev = device_prefill_inputs(case)
+    say("prefill paired schedule", T, H, G)
+    first = run_prefill(case, dev=dev)
+    second = run_prefill(case, dev=dev)
+    assert torch.equal(first, second)
+    check(to_f64(first), oracle_prefill(case), W.BF16, case.name)
+
+
 def test_deterministic_and_causal():
     case = W.make_prefill("inv", 31, lengths=[333], H=16, G=4, d=128)
     dev = device_prefill_inputs(case)
