@@ -503,9 +503,9 @@ gqa_status gqa_prefill(const void* q, const void* k, const void* v, const int32_
   }
   // the paired schedule: grids of the unmasked causal kernel that are resident at once (two
   // workgroups per CU), whose heaviest blocks see at least 48 key tiles (measured: T = 4096
-  // and 8192 7-8% faster, T = 2048 the same, T = 1024 10% slower: the light workgroup's
-  // second start outweighs the tiles it takes; a grid of 584 workgroups 25% slower: light
-  // workgroups that wait for a slot take their share of the heavy block last)
+  // and 3072 (H = 16, G = 8) 8-11% faster, T = 2048 the same, T = 1024 10% slower: the light
+  // workgroup's second start outweighs the tiles it takes; a grid of 584 workgroups 25%
+  // slower: light workgroups that wait for a slot take their share of the heavy block last)
   const bool paired = bf16 && zigzag && causal && pairs > 0 && p->window <= 0 && !p->block_mask &&
                       (T + 63) / 64 >= 48 && (long)B * G * n_blk <= 2L * n_cu;
   int32_t* counters = claim;
