@@ -485,8 +485,9 @@ gqa_status gqa_prefill(const void* q, const void* k, const void* v, const int32_
   const long cols = (long)T * (H / G);
   const int cpb = gqa::prefill_bf16_cols_per_block();
   const int n_blk = (int)((cols + cpb - 1) / cpb);
-  // Pair heavy and light causal blocks when the grid is at most about two workgroups per CU
-  // (two bf16 prefill workgroups are resident per CU); longer grids run heaviest first, and
+  // Pair heavy and light causal blocks when the grid is at most 2.5 workgroups per CU (two
+  // bf16 prefill workgroups are resident per CU; measured against heaviest first: 1-2% faster
+  // at 584 and 640 workgroups, 5-12% slower at 704-1024); longer grids run heaviest first, and
   // when a group's blocks spread over several XCDs (G < 8) the workgroups of the unmasked
   // kernel claim their ranks (the counters are zeroed by the prologue launch before it).
   // Measured on T = 32768, H = 64 on two boxes: G = 1 1.4-1.7% faster, G = 4 0.2-0.8%; the
@@ -499,7 +500,7 @@ gqa_status gqa_prefill(const void* q, const void* k, const void* v, const int32_
         hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return GQA_EHIP;
     const long grid = (long)B * G * n_blk;
-    zigzag = (causal && !p->cu_seqlens && grid <= 4L * n_cu) ? 1 : 0;
+    zigzag = (causal && !p->cu_seqlens && 2 * grid <= 5L * n_cu) ? 1 : 0;
   }
   // the paired schedule: grids of the unmasked causal kernel that are resident at once (two
   // workgroups per CU), whose heaviest blocks see at least 48 key tiles (measured: T = 4096

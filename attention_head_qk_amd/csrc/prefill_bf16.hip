@@ -719,32 +719,42 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
       // another XCD), laid out so that each store instruction of a wave writes 1 KB in one
       // piece; then count the part in. The part counted second reads the other one back and
       // merges, the heavy block's own part always as the first operand, so the bits do not
-      // depend on which part ends last.
+      // depend on which part ends last. The heavy workgroup's part usually ends last, so it
+      // looks at the count first: when its partner's part is in, it merges at once and its
+      // own part is never stored.
       constexpr int PF = COLS * D + 2 * COLS;  // floats of one part
       constexpr int kCoherent = 16;            // cache policy: sc1 (device-coherent access)
       const __amdgpu_buffer_rsrc_t prs = make_rsrc(a.pair_part + (long)pair * 2 * PF, 2 * PF * 4);
       const int mine = slot * PF * 4, other = (1 - slot) * PF * 4;  // byte offsets of the parts
       const int cw = wave * 32 + l32;  // column inside the block
       auto o_off = [&](int mt, int r4) { return ((((mt * 4 + r4) * 2 + grp) * COLS + cw) * 4) * 4; };
-#pragma unroll
-      for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4_t v = {o[mt][4 * r4], o[mt][4 * r4 + 1], o[mt][4 * r4 + 2], o[mt][4 * r4 + 3]};
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), prs, mine + o_off(mt, r4), 0,
-                                                 kCoherent);
-        }
-      if (grp == 0) {
-        const f32x2_t ml = {m_run, l_tot};
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, ml), prs,
-                                              mine + (COLS * D + 2 * cw) * 4, 0, kCoherent);
+      int partner_in = 0;
+      if (slot == 0) {
+        if (tid == 0) s_arrived = __hip_atomic_load(a.pair_arrive + pair, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        partner_in = __builtin_amdgcn_readfirstlane(s_arrived);
       }
-      wait_vmem();
-      __syncthreads();
-      if (tid == 0)
-        s_arrived = __hip_atomic_fetch_add(a.pair_arrive + pair, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __syncthreads();
-      if (__builtin_amdgcn_readfirstlane(s_arrived) == 0) return;  // the other part merges
+      if (partner_in == 0) {
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4_t v = {o[mt][4 * r4], o[mt][4 * r4 + 1], o[mt][4 * r4 + 2], o[mt][4 * r4 + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), prs, mine + o_off(mt, r4), 0,
+                                                   kCoherent);
+          }
+        if (grp == 0) {
+          const f32x2_t ml = {m_run, l_tot};
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, ml), prs,
+                                                mine + (COLS * D + 2 * cw) * 4, 0, kCoherent);
+        }
+        wait_vmem();
+        __syncthreads();
+        if (tid == 0)
+          s_arrived = __hip_atomic_fetch_add(a.pair_arrive + pair, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        if (__builtin_amdgcn_readfirstlane(s_arrived) == 0) return;  // the other part merges
+      }
       const f32x2_t mlo = __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(
           prs, other + (COLS * D + 2 * cw) * 4, 0, kCoherent));
       const float mA = slot == 0 ? m_run : mlo[0], mB = slot == 0 ? mlo[0] : m_run;
