@@ -53,10 +53,11 @@ def test_long_32k_sampled_rows(G):
     say(case.name, len(rows), "rows", stats)
 
 
-@pytest.mark.parametrize("T,H,G", [(8192, 32, 2), (6000, 48, 3)])
+@pytest.mark.parametrize("T,H,G", [(8192, 32, 2), (6000, 48, 3), (3072, 32, 4)])
 def test_claimed_ranks_sampled_rows(T, H, G):
-    # grids of more than two rounds whose groups each span several XCDs (G < 8): the
+    # grids of more than 2.5 rounds whose groups each span several XCDs (G < 8): the
     # workgroups take their ranks from the per-group counters instead of their block ids
+    # (T = 3072, H = 32, G = 4: 768 workgroups, just past the heavy/light pairing)
     import _oracle_pool as OP
     case = W.make_prefill(f"claims_T{T}_H{H}_G{G}", 131 + G, lengths=[T], H=H, G=G, d=128)
     say("prefill with claimed ranks", T, H, G)
