@@ -87,6 +87,37 @@ SHAPES = [
 ]
 
 
+def _random_shapes(n, seed):
+    """n seeded draws of (lengths, H, G, d, causal): 1-4 sequences of 0-400 tokens (packed, or
+    dense when the lengths agree), G in {1, 2, 4, 8}, h in {1, 2, 3, 4, 5, 8, 16} (H <= 64),
+    d in {64, 128}, causal 4 times in 5."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    while len(shapes) < n:
+        G = int(rng.choice([1, 2, 4, 8]))
+        h = int(rng.choice([1, 2, 3, 4, 5, 8, 16]))
+        if G * h > 64:
+            continue
+        B = int(rng.integers(1, 5))
+        lengths = [int(x) for x in rng.integers(0, 401, size=B)]
+        if rng.random() < 0.25:
+            lengths = [lengths[0]] * B
+        if max(lengths) == 0:
+            lengths[0] = 1
+        shapes.append((lengths, G * h, G, int(rng.choice([64, 128])), bool(rng.random() < 0.8)))
+    return shapes
+
+
+@pytest.mark.parametrize("lengths,H,G,d,causal", _random_shapes(16, 2024))
+def test_random_shapes_full(lengths, H, G, d, causal):
+    # seeded combinations of the shape parameters beyond the hand-picked list, every element
+    case = W.make_prefill(f"random_{lengths}_{H}_{G}_{d}_{causal}", 17 + H + G + d + len(lengths),
+                          lengths=lengths, H=H, G=G, d=d, causal=causal)
+    say("prefill", case.name)
+    got = to_f64(run_prefill(case))
+    check(got, oracle_prefill(case), W.BF16, case.name)
+
+
 @pytest.mark.parametrize("lengths,H,G,d,causal", SHAPES)
 def test_small_shapes_full(lengths, H, G, d, causal):
     case = W.make_prefill(f"small_{lengths}_{H}_{G}_{d}_{causal}", 11 + H + G + d,
@@ -218,14 +249,22 @@ def test_default_positions_and_k_out():
     assert np.all(err <= 2.0 ** -8 * np.abs(kt) + 1e-6)
 
 
-@pytest.mark.parametrize("T,H,G", [(4096, 16, 8), (3100, 24, 8), (4000, 8, 2)])
-def test_paired_schedule(T, H, G):
+@pytest.mark.parametrize("lengths,H,G,d", [
+    ([4096], 16, 8, 128),
+    ([3100], 24, 8, 128),        # 584 workgroups: past the pairing, zigzag order only
+    ([4000], 8, 2, 128),         # 125 blocks per group: the middle block has no partner
+    ([3072], 16, 8, 64),         # d = 64
+    ([3072, 3072], 8, 4, 128),   # a dense batch of two: pairs within each sequence
+])
+def test_paired_schedule(lengths, H, G, d):
     # one-round grids whose heavy blocks share their key tiles with their light partners
     # (fixed cut, partial states merged by whichever part ends last): every element against
     # the oracle, and bit-identical on a second run
-    case = W.make_prefill(f"paired_T{T}_H{H}_G{G}", 141 + H + G, lengths=[T], H=H, G=G, d=128)
+    case = W.make_prefill(f"paired_{lengths}_H{H}_G{G}_d{d}", 141 + H + G + d, lengths=lengths,
+                          H=H, G=G, d=d)
+    assert case.dense
     dev = device_prefill_inputs(case)
-    say("prefill paired schedule", T, H, G)
+    say("prefill paired schedule", lengths, H, G, d)
     first = run_prefill(case, dev=dev)
     second = run_prefill(case, dev=dev)
     assert torch.equal(first, second)
