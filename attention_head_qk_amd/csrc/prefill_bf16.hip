@@ -38,8 +38,11 @@
 //   subtraction nor an O rescale; the result is unchanged because softmax does not depend on
 //   the subtracted constant.
 // * Scheduling. Blocks are issued heaviest first (descending position) so the causal
-//   triangle drains without a long tail; when the whole grid fits on the chip in about two
-//   rounds, heavy and light blocks are paired instead (zigzag). The group index is the
+//   triangle drains without a long tail; when the whole grid fits on the chip in at most 2.5
+//   rounds, heavy and light blocks are paired instead (zigzag), and when it fits at once
+//   (and its heaviest blocks are long) the light block of a pair also takes a fixed share of
+//   its heavy partner's key tiles, the two partial softmax states merged in a fixed order
+//   (the paired schedule, template parameter PAIR). The group index is the
 //   fastest-varying part of the block id, which keeps the blocks of one KV group on the same
 //   XCD (blocks are dealt round-robin over the 8 XCDs) when G is a multiple of 8, so its K/V
 //   stay in that XCD's L2; with several sequences the ranks go in runs of 32 per sequence, so
