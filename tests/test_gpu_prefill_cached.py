@@ -41,8 +41,35 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("lengths,cache_lens,max_seq,H,G,d,causal", SHAPES)
+def _random_cached_shapes(n, seed):
+    """n seeded draws of (lengths, cache_lens, max_seq, H, G, d, causal): 1-4 sequences with
+    chunks of 0-300 new tokens after caches of 0-700 rows (packed, or dense when the chunk
+    lengths agree), max_seq 0-100 rows above the longest, G in {1, 2, 4, 8}, h in
+    {1, 2, 3, 4, 8, 16} (H <= 64), d in {64, 128}, causal 4 times in 5."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    while len(shapes) < n:
+        G = int(rng.choice([1, 2, 4, 8]))
+        h = int(rng.choice([1, 2, 3, 4, 8, 16]))
+        if G * h > 64:
+            continue
+        B = int(rng.integers(1, 5))
+        lengths = [int(x) for x in rng.integers(0, 301, size=B)]
+        if rng.random() < 0.25:
+            lengths = [lengths[0]] * B
+        if max(lengths) == 0:
+            lengths[0] = 1
+        cache_lens = [int(x) for x in rng.integers(0, 701, size=B)]
+        max_seq = max(c + t for c, t in zip(cache_lens, lengths)) + int(rng.integers(0, 101))
+        shapes.append((lengths, cache_lens, max_seq, G * h, G, int(rng.choice([64, 128])),
+                       bool(rng.random() < 0.8)))
+    return shapes
+
+
+@pytest.mark.parametrize("lengths,cache_lens,max_seq,H,G,d,causal",
+                         SHAPES + _random_cached_shapes(10, 404))
 def test_small_cached_full(lengths, cache_lens, max_seq, H, G, d, causal):
+    # the hand-picked shapes, then seeded random ones
     case = W.make_cached_prefill(f"cached_{lengths}_{cache_lens}", 90 + H + G + d, lengths,
                                  cache_lens, max_seq, H=H, G=G, d=d, causal=causal)
     say("prefill cached", case.name, max_seq, H, G, d, causal)
