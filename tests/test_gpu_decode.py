@@ -65,6 +65,42 @@ def test_decode_edge_lengths(dtype, H, G, d, max_seq):
         check(out[b], want, dtype, f"L={L}")
 
 
+def _random_decode_shapes(n, seed):
+    """n seeded draws of (B, max_seq, lengths, H, G, d, dtype, append): 1-16 sequences, a
+    cache of 1-6000 rows with lengths uniform in [0, max_seq], G in {1, 2, 4, 8}, h in
+    {1, 2, 3, 4, 6, 8, 12, 16, 32, 40} (H <= 128), d in {64, 128}, bf16 3 times in 4, the
+    K/V append 4 times in 5."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    while len(shapes) < n:
+        G = int(rng.choice([1, 2, 4, 8]))
+        h = int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16, 32, 40]))
+        if G * h > 128:
+            continue
+        B = int(rng.integers(1, 17))
+        max_seq = int(rng.integers(1, 6001))
+        lens = [int(x) for x in rng.integers(0, max_seq + 1, size=B)]
+        shapes.append((B, max_seq, lens, G * h, G, int(rng.choice([64, 128])),
+                       W.BF16 if rng.random() < 0.75 else W.F32, bool(rng.random() < 0.8)))
+    return shapes
+
+
+@pytest.mark.parametrize("B,max_seq,lens,H,G,d,dtype,append", _random_decode_shapes(18, 808))
+def test_decode_random_shapes(B, max_seq, lens, H, G, d, dtype, append):
+    # seeded shapes beyond the edge-length grid: every sequence against the oracle
+    case = W.make_decode("rand", 91 + H + G + d + B, B=B, max_seq=max_seq, H=H, G=G, d=d,
+                         dtype=dtype, seq_lens=lens)
+    say("decode random", B, max_seq, H, G, d, dtype, append)
+    dev = device_decode_inputs(case, fill_invalid=float("nan"))
+    out = to_f64(run_decode(case, dev, append=append))
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.array_equal(out[b], np.zeros((H, d))), "empty sequence must give zeros"
+            continue
+        want, _, _ = oracle_decode_seq(case, b, append=append)
+        check(out[b], want, dtype, f"b={b} L={L}")
+
+
 def test_decode_without_append_and_explicit_positions():
     case = W.make_decode("noappend", 71, B=5, max_seq=2048, H=16, G=4, d=128,
                          seq_lens=[700, 1, 2048, 513, 64])
