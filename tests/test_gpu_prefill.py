@@ -171,6 +171,15 @@ def test_small_shapes_f32(lengths, H, G, d, causal):
     check(to_f64(run_prefill(case)), oracle_prefill(case), W.F32, case.name)
 
 
+@pytest.mark.parametrize("lengths,H,G,d,causal", _random_shapes(8, 4242))
+def test_random_shapes_f32(lengths, H, G, d, causal):
+    # the fp32 path on seeded shapes, every element within the fp32 bound
+    case = W.make_prefill("f32_random", 7 + H + G + d, lengths=lengths, H=H, G=G, d=d,
+                          causal=causal, dtype=W.F32)
+    say("prefill f32 random", lengths, H, G, d, causal)
+    check(to_f64(run_prefill(case)), oracle_prefill(case), W.F32, case.name)
+
+
 def test_peaky_softmax():
     # gamma x 8 drives every row towards one-hot (Qwen3 series 1, D1-4 Q8); scores reach
     # ~1e3 in magnitude. The bf16 rounding of q~ and k~ moves such a score by about |s| 2^-8
