@@ -239,6 +239,18 @@ def test_workspace_bytes():
     assert ws(_lib.GQA_OP_PREFILL, 1, 3, 1, 1, 64, _lib.GQA_BF16) == 512 + 256 + part(1, 64)
     # a grid of more than 512 workgroups (T=32768, h=16: 4096 blocks x 4 groups): no pairs
     assert ws(_lib.GQA_OP_PREFILL, 1, 32768, 64, 4, 128, _lib.GQA_BF16) == 32768 * 4 * 256 + 256
+    # the boundary: T=4097 gives 65 blocks per group, 520 workgroups: no pairs; a dense batch
+    # of two at T=2048 (2 x 8 x 32 = 512 workgroups) keeps them, 16 blocks' pairs per sequence
+    def up(n):
+        return -(-n // 256) * 256
+    assert ws(_lib.GQA_OP_PREFILL, 1, 4097, 16, 8, 128, _lib.GQA_BF16) == (
+        up(4097 * 8 * 128 * 2) + 256)
+    assert ws(_lib.GQA_OP_PREFILL, 2, 2048, 16, 8, 128, _lib.GQA_BF16) == (
+        2 * 2048 * 8 * 128 * 2 + up((8 + 2 * 8 * 16) * 4) + part(2 * 8 * 16, 128))
+    # odd block counts round the pairs up (the middle block has no partner): T=4000, h=4
+    # gives 125 blocks per group, 63 pairs
+    assert ws(_lib.GQA_OP_PREFILL, 1, 4000, 8, 2, 128, _lib.GQA_BF16) == (
+        up(4000 * 2 * 128 * 2) + up((2 + 2 * 63) * 4) + part(2 * 63, 128))
     # decode: q~ + fp32 partial O + fp32 (m, l) per split + two [B] step-length buffers
     S = lib.gqa_decode_split_keys(64, 32, 8, 32768)
     assert S == 1024
