@@ -67,6 +67,17 @@ MUTATIONS = [
      "vis &= bm[i // block, j // block]"),
     ("block layout transposed", "vis &= bm[i // block, j // block] | (i // block == j // block)",
      "vis &= bm[j // block, i // block] | (i // block == j // block)"),
+    ("softmax without the row maximum", "    E = np.exp(S - m)\n", "    E = np.exp(S)\n"),
+    ("decode head i reads group i mod G",
+     "        g = i // h\n        p = attention_weights(qt[i:i + 1]",
+     "        g = i % G\n        p = attention_weights(qt[i:i + 1]"),
+    ("decode appends K without its norm",
+     "k_slot = rope(rms_norm(np.asarray(k_new, np.float64)[None], k_norm_w, eps),",
+     "k_slot = rope(np.asarray(k_new, np.float64)[None],"),
+    ("decode query rotated at position 0",
+     "qt = rope(rms_norm(np.asarray(q_b, np.float64)[None], q_norm_w, eps), np.array([pos]),",
+     "qt = rope(rms_norm(np.asarray(q_b, np.float64)[None], q_norm_w, eps), np.array([0]),"),
+    ("decode keeps the stale V slot", "        vc[slot] = v_slot\n", "        pass\n"),
     ("sampled rows ignore the window",
      "vis = visible_keys(len(r_in[c]), Tk, causal, window, block_mask, block,",
      "vis = visible_keys(len(r_in[c]), Tk, causal, 0, block_mask, block,"),
