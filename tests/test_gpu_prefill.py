@@ -264,6 +264,7 @@ def test_default_positions_and_k_out():
     ([4000], 8, 2, 128),         # 125 blocks per group: the middle block has no partner
     ([3072], 16, 8, 64),         # d = 64
     ([3072, 3072], 8, 4, 128),   # a dense batch of two: pairs within each sequence
+    ([4000], 8, 8, 128),         # h = 1: a column block spans 128 positions, two key tiles
 ])
 def test_paired_schedule(lengths, H, G, d):
     # one-round grids whose heavy blocks share their key tiles with their light partners
