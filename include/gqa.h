@@ -149,7 +149,9 @@ void gqa_params_init(gqa_params *p);
  *     further; key tiles no query of a workgroup sees are skipped.  GQA_EINVAL for a
  *     negative window, a window without the causal mask, a misaligned block_mask or
  *     block_mask_words too small for T; GQA_ENOTSUP for either with fp32.
- *   Needs p->workspace of gqa_workspace_bytes(GQA_OP_PREFILL, B, T, H, G, d, dtype). */
+ *   Needs p->workspace of gqa_workspace_bytes(GQA_OP_PREFILL, B, T, H, G, d, dtype).  The
+ *   call keeps counters and, on grids that fit the chip at once, partial softmax states in
+ *   it (reset by the call itself): calls that share one workspace must not overlap. */
 gqa_status gqa_prefill(const void *q, const void *k, const void *v, const int32_t *positions,
                        void *out, int B, int T, int H, int G, int d, int causal,
                        const gqa_params *p);
@@ -184,7 +186,9 @@ gqa_status gqa_prefill_cached(const void *q, const void *k, const void *v, void 
  *   p->window and p->block_mask are not supported here (GQA_ENOTSUP when set).
  *   When the two caches together exceed 512 MiB (2*B*max_seq*G*d*elem bytes) the bf16 pass
  *   reads V with a non-temporal cache hint; the results are the same bits either way.
- *   Needs p->workspace of gqa_workspace_bytes(GQA_OP_DECODE, B, max_seq, H, G, d, dtype). */
+ *   Needs p->workspace of gqa_workspace_bytes(GQA_OP_DECODE, B, max_seq, H, G, d, dtype), where
+ *   the split partials live until the combine: calls that share one workspace must not
+ *   overlap. */
 gqa_status gqa_decode(const void *q, void *k_cache, void *v_cache, const int32_t *seq_lens,
                       void *out, int B, int H, int G, int d, int max_seq,
                       const gqa_params *p);
