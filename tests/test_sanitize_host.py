@@ -102,7 +102,7 @@ def test_abi_suite_under_sanitizers(san_lib, tmp_path):
     # the sanitizer runtime must come first; anything already preloaded stays after it
     env["LD_PRELOAD"] = rt + (":" + os.environ["LD_PRELOAD"] if os.environ.get("LD_PRELOAD") else "")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_abi.py", "-k", "not c_client"],
+                        "tests/test_abi.py", "tests/test_abi_sweep.py", "-k", "not c_client"],
                        cwd=tmp_path, capture_output=True, text=True, env=env, timeout=600)
     assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-5000:]
     assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr[-5000:]
