@@ -87,3 +87,53 @@ def test_decode_host_checks_sweep(B, S, H, G, d, dtype, window, ws, ws_bytes, q,
         assert B == 0
     if B < 0 or S <= 0 or window != 0:
         assert r in REJECTED
+
+
+@SWEEP
+@given(B=sizes, T=sizes, S=sizes, H=heads, G=heads, d=st.sampled_from([-1, 64, 96, 128]),
+       causal=st.integers(-1, 2), dtype=st.sampled_from([-1, 0, 1, 7]),
+       window=st.sampled_from([-1, 0, 3]), cl=st.sampled_from([None, A, A + 2]), q=ptrs,
+       kc=ptrs, out=ptrs, cu=st.sampled_from([None, A, A + 2]))
+def test_prefill_cached_host_checks_sweep(B, T, S, H, G, d, causal, dtype, window, cl, q, kc, out,
+                                          cu):
+    p = _params(dtype, window, None, 0, None, 0, cu)
+    r = _lib.load().gqa_prefill_cached(q, A, A, kc, A, cl, None, out, B, T, H, G, d, S, causal,
+                                       ctypes.byref(p))
+    assert r in STATUS
+    if r == _lib.GQA_OK:
+        assert B == 0 or T == 0
+    if B < 0 or T < 0 or causal not in (0, 1) or dtype == _lib.GQA_F32:
+        assert r in REJECTED
+
+
+@SWEEP
+@given(N=sizes, H=heads, G=heads, d=st.sampled_from([-1, 0, 64, 96, 128]),
+       dtype=st.sampled_from([-1, 0, 1, 7]), q=ptrs, k=ptrs, qo=ptrs, ko=ptrs,
+       pos=st.sampled_from([None, A, A + 2]))
+def test_qk_norm_rope_host_checks_sweep(N, H, G, d, dtype, q, k, qo, ko, pos):
+    p = _params(dtype, 0, None, 0, None, 0)
+    r = _lib.load().gqa_qk_norm_rope(q, k, pos, qo, ko, N, H, G, d, ctypes.byref(p))
+    assert r in STATUS
+    if r == _lib.GQA_OK:
+        assert N == 0
+    if N < 0:
+        assert r in REJECTED
+
+
+@SWEEP
+@given(B=sizes, S=sizes, H=heads, G=heads, d=st.sampled_from([-1, 64, 128]),
+       steps=st.sampled_from([-1, 0, 1, 2, 256, 257]), dtype=st.sampled_from([0, 1, 7]),
+       q=ptrs, sl=st.sampled_from([None, A, A + 2]), out=ptrs,
+       append=st.sampled_from([(A, A), (None, None), (A, None)]))
+def test_decode_graph_host_checks_sweep(B, S, H, G, d, steps, dtype, q, sl, out, append):
+    p = _params(dtype, 0, None, 0, A, 1 << 62)
+    p.k_new, p.v_new = append
+    g = ctypes.c_void_p()
+    lib = _lib.load()
+    r = lib.gqa_decode_graph_create_steps(q, A, A, sl, out, B, H, G, d, S, steps,
+                                          ctypes.byref(p), ctypes.byref(g))
+    assert r in STATUS
+    if r == _lib.GQA_OK:
+        lib.gqa_decode_graph_destroy(g)
+    if B < 0 or S <= 0 or not 1 <= steps <= 256:
+        assert r in REJECTED
