@@ -81,7 +81,15 @@ def test_decode_host_checks_sweep(B, S, H, G, d, dtype, window, ws, ws_bytes, q,
     p = _params(dtype, window, None, 0, ws, ws_bytes)
     if append is not None:
         p.k_new, p.v_new = append
-    r = _lib.load().gqa_decode(q, kc, vc, sl, out, B, H, G, d, S, ctypes.byref(p))
+    lib = _lib.load()
+    r = lib.gqa_decode(q, kc, vc, sl, out, B, H, G, d, S, ctypes.byref(p))
+    assert r in STATUS
+    if r == _lib.GQA_OK:
+        assert B == 0
+    if B < 0 or S <= 0 or window != 0:
+        assert r in REJECTED
+    # the entry point without a workspace: same checks, its own size limit instead
+    r = lib.gqa_decode_noalloc(q, kc, vc, sl, out, B, H, G, d, S, ctypes.byref(p))
     assert r in STATUS
     if r == _lib.GQA_OK:
         assert B == 0
