@@ -101,6 +101,25 @@ def test_decode_random_shapes(B, max_seq, lens, H, G, d, dtype, append):
         check(out[b], want, dtype, f"b={b} L={L}")
 
 
+def test_decode_at_the_split_limit():
+    # The largest decode the combine pass takes at G = 1: 1024-key splits, at most 4096 of
+    # them per sequence, so a 4194304-row cache (1 GiB of K, 1 GiB of V at d = 128); one
+    # sequence fills it (the newest key appended at the last slot), the next stops one short.
+    import attention_head_qk_amd as gqa
+    B, max_seq, H, G, d = 2, 4194304, 8, 1, 128
+    assert gqa.decode_split_keys(B, H, G, max_seq) * 4096 == max_seq
+    lens = [max_seq, max_seq - 1]
+    case = W.make_decode("splitlimit", 97, B=B, max_seq=max_seq, H=H, G=G, d=d, seq_lens=lens)
+    say("decode at the split limit", max_seq)
+    dev = device_decode_inputs(case)
+    out = to_f64(run_decode(case, dev))
+    del dev
+    torch.cuda.empty_cache()
+    for b, L in enumerate(lens):
+        want, _, _ = oracle_decode_seq(case, b)
+        check(out[b], want, W.BF16, f"b={b} L={L}")
+
+
 def test_decode_without_append_and_explicit_positions():
     case = W.make_decode("noappend", 71, B=5, max_seq=2048, H=16, G=4, d=128,
                          seq_lens=[700, 1, 2048, 513, 64])

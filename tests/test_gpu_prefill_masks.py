@@ -153,6 +153,42 @@ def test_window_and_block_mask_full(lengths, H, G):
     check(got, oracle_prefill(case, window=150, block_mask=bm), W.BF16, case.name)
 
 
+def test_window_at_maximum_length_sampled_rows():
+    # The longest sequence the bf16 kernel takes at G = 1, d = 128: it addresses a group's K/V
+    # rows with 32-bit byte offsets, so T * G * d * 2 < 2^31, T = 8388607 (h = 2: 16.8 M
+    # columns). A 512-key window keeps the work linear. The inputs repeat one seeded
+    # 65536-token block (RoPE positions still run 0 .. T - 1, so no two windows see the same
+    # rotated keys); each sampled row is checked against the oracle on the 512 keys it sees,
+    # passed as a sequence of its own at their true positions.
+    import dataclasses
+    T, P, window = 8388607, 1 << 16, 512
+    base = W.make_prefill("maxlen_block", 191, lengths=[P], H=2, G=1, d=128)
+    reps = -(-T // P)
+
+    def tile(a):
+        return np.ascontiguousarray(np.tile(a, (reps, 1, 1))[:T])
+
+    case = dataclasses.replace(base, name="maxlen_window", lengths=np.array([T]),
+                               q=tile(base.q), k=tile(base.k), v=tile(base.v),
+                               positions=np.arange(T, dtype=np.int32),
+                               cu_seqlens=np.array([0, T], dtype=np.int32))
+    say("prefill window 512 at the maximum length", T)
+    rows = [0, 511, 512, 4096, 1 << 22, (1 << 22) + 63, (1 << 22) + 64, (1 << 23) - 1000,
+            T - 65, T - 64, T - 63, T - 2, T - 1]
+    out = run_prefill(case, window=window)
+    got = to_f64(out[rows])
+    del out
+    torch.cuda.empty_cache()
+    for r, g in zip(rows, got):
+        lo = max(0, r - window + 1)
+        n = r + 1 - lo
+        sub = dataclasses.replace(case, name=f"row {r}", lengths=np.array([n]), q=case.q[lo:r + 1],
+                                  k=case.k[lo:r + 1], v=case.v[lo:r + 1],
+                                  positions=np.arange(lo, r + 1, dtype=np.int32),
+                                  cu_seqlens=np.array([0, n], dtype=np.int32))
+        check(g[None], oracle_prefill(sub, window=window)[-1:], W.BF16, f"row {r}")
+
+
 def test_window_4k_full():
     case = W.prefill_4k()
     say("prefill window 512 at T=4096")
