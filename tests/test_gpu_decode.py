@@ -120,6 +120,30 @@ def test_decode_at_the_split_limit():
         check(out[b], want, W.BF16, f"b={b} L={L}")
 
 
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_decode_batch_at_the_grid_limit(dtype):
+    # 65535 sequences, the most a decode takes (sequences index a grid dimension), with
+    # caches of 0-8 rows
+    B, max_seq = 65535, 8
+    lens = np.random.default_rng(5).integers(0, max_seq + 1, size=B)
+    case = W.make_decode("gridlimit", 98, B=B, max_seq=max_seq, H=4, G=2, d=64, dtype=dtype,
+                         seq_lens=lens)
+    say("decode at the grid limit", dtype, B)
+    dev = device_decode_inputs(case)
+    out = to_f64(run_decode(case, dev))
+    from oracle import gqa_oracle as O
+    q, kn, vn = case.f64("q"), case.f64("k_new"), case.f64("v_new")
+    gq, gk = case.f64("q_norm_w"), case.f64("k_norm_w")
+    want = np.zeros_like(out)
+    for b, L in enumerate(lens):
+        if L:
+            k, v = case.cache_rows(b)
+            want[b] = O.decode_one(q[b], W.to_f64(k, dtype), W.to_f64(v, dtype), int(L), gq, gk,
+                                   case.eps, case.theta, k_new=kn[b], v_new=vn[b])[0]
+    assert np.array_equal(out[lens == 0], want[lens == 0])  # empty sequences give zeros
+    check(out, want, dtype, case.name)
+
+
 def test_decode_without_append_and_explicit_positions():
     case = W.make_decode("noappend", 71, B=5, max_seq=2048, H=16, G=4, d=128,
                          seq_lens=[700, 1, 2048, 513, 64])

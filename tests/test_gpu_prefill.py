@@ -180,6 +180,18 @@ def test_random_shapes_f32(lengths, H, G, d, causal):
     check(to_f64(run_prefill(case)), oracle_prefill(case), W.F32, case.name)
 
 
+@pytest.mark.parametrize("dtype", [W.F32, W.BF16])
+def test_batch_at_the_grid_limit(dtype):
+    # 65535 one- or two-token sequences: the fp32 kernel puts the sequence on a grid dimension
+    # of at most 65535 entries (the largest batch it takes), the bf16 one numbers B * G * n_blk
+    # workgroups along one dimension; every element against the oracle
+    B = 65535
+    lengths = [2] * B if dtype == W.BF16 else [1] * B
+    case = W.make_prefill(f"gridlimit_{dtype}", 23, lengths=lengths, H=4, G=2, d=64, dtype=dtype)
+    say("prefill at the grid limit", dtype, B)
+    check(to_f64(run_prefill(case)), oracle_prefill(case), dtype, case.name)
+
+
 def test_peaky_softmax():
     # gamma x 8 drives every row towards one-hot (Qwen3 series 1, D1-4 Q8); scores reach
     # ~1e3 in magnitude. The bf16 rounding of q~ and k~ moves such a score by about |s| 2^-8
