@@ -144,6 +144,19 @@ def test_decode_batch_at_the_grid_limit(dtype):
     check(out, want, dtype, case.name)
 
 
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_decode_most_heads(dtype):
+    # H = 4096 query heads on one KV head (h = 4096, the most heads taken)
+    lens = [1, 300, 2048]
+    case = W.make_decode("mostheads", 99, B=3, max_seq=2048, H=4096, G=1, d=64, dtype=dtype,
+                         seq_lens=lens)
+    say("decode most heads", dtype)
+    out = to_f64(run_decode(case, device_decode_inputs(case)))
+    for b, L in enumerate(lens):
+        want, _, _ = oracle_decode_seq(case, b)
+        check(out[b], want, dtype, f"b={b} L={L}")
+
+
 def test_decode_without_append_and_explicit_positions():
     case = W.make_decode("noappend", 71, B=5, max_seq=2048, H=16, G=4, d=128,
                          seq_lens=[700, 1, 2048, 513, 64])

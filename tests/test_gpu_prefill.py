@@ -80,6 +80,7 @@ SHAPES = [
     ([150], 64, 1, 128, True),      # MQA, h = 64
     ([77], 128, 1, 128, True),      # h = 128: one position per column block
     ([97], 256, 1, 128, True),      # h = 256 > columns per block
+    ([5], 4096, 1, 64, True),       # H = 4096, the most heads taken: h = 4096
     ([190], 16, 8, 64, True),       # d = 64
     ([130], 32, 8, 128, False),     # no causal mask
     ([1, 63, 64, 65, 0, 129, 7], 32, 8, 128, True),  # packed, ragged, an empty sequence
