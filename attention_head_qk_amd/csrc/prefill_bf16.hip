@@ -85,7 +85,7 @@ __device__ __forceinline__ u32x2_t ds_read_tr16(const char* lds) {
 // MASK: bit 0 = sliding window (a.window), bit 1 = 64-key block layout (a.block_mask).
 // CACHE: keys come from caches after a.cache_lens[b] earlier rows (cached prefill).
 template <int D, int MASK, bool CACHE, bool PAIR>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, D == 64 && !PAIR ? 3 : 2) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int DCH = D / 8;               // 16-byte chunks per K row
   constexpr int NST = D / 16;              // k-steps of S^T = K Q^T
   constexpr int NMT = D / 32;              // 32-row tiles of O^T
@@ -781,20 +781,42 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a) {
       }
     }
   }
+  // Output rows go out through LDS: straight from the accumulator layout every store
+  // instruction would write 16-byte pieces of 32 different rows; staged, each writes 64 / DCH
+  // whole rows. The wave writes its 32 columns as bf16 rows [column][d] (16-byte chunks
+  // XOR-swizzled by column) into half of a K tile buffer, which nothing reads after the last
+  // step's barrier, and reads them back row by row.
   const float inv = 1.0f / l_tot;
-  if (cvalid) {
-    bf16_t* op = reinterpret_cast<bf16_t*>(a.out) + ((long)(seq0 + pcol) * a.H + head) * D;
+  char* const stg = (wave < 2 ? kbuf0 : kbuf1) + (wave & 1) * (32 * D * 2);
+  static_assert(2 * 32 * D * 2 <= KBYTES, "two waves' rows fit one K tile buffer");
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
+  for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = 32 * mt + 8 * r4 + 4 * grp;
-        u32x2_t w = {pack_bf16x2(o[mt][4 * r4 + 0] * inv, o[mt][4 * r4 + 1] * inv),
-                     pack_bf16x2(o[mt][4 * r4 + 2] * inv, o[mt][4 * r4 + 3] * inv)};
-        *reinterpret_cast<u32x2_t*>(op + d0) = w;
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int ch = 4 * mt + r4;  // 16-byte chunk of d = 32 mt + 8 r4 + [0, 8)
+      const u32x2_t w = {pack_bf16x2(o[mt][4 * r4 + 0] * inv, o[mt][4 * r4 + 1] * inv),
+                         pack_bf16x2(o[mt][4 * r4 + 2] * inv, o[mt][4 * r4 + 3] * inv)};
+      *reinterpret_cast<u32x2_t*>(stg + l32 * D * 2 + ((ch ^ (l32 % DCH)) * 16) + 8 * grp) = w;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  {
+    constexpr int RPI = 64 / DCH;  // rows per store instruction
+    const int rl = lane / DCH, ch = lane % DCH;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int c = i * RPI + rl;  // column inside the wave
+      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(stg + c * D * 2 + ((ch ^ (c % DCH)) * 16));
+      const int mc = wcol + c;
+      if (mc < ncol) {
+        const int p = (int)((unsigned)mc / (unsigned)h);
+        const long row = (long)(seq0 + p) * a.H + g * h + (mc - p * h);
+        *reinterpret_cast<u32x4_t*>(reinterpret_cast<bf16_t*>(a.out) + row * D + 8 * ch) = val;
       }
     }
   }
+  // the light workgroup of a pair runs a second block, whose first DMA refills these buffers
+  if constexpr (PAIR) __syncthreads();
   };  // run
 
   if constexpr (PAIR) {
