@@ -47,7 +47,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-FP32_PEAK_TFLOPS = 157.3
+FP32_PEAK_TFLOPS = 157.3    # vector fp32: 256 CUs x 128 FMA lanes per clock x 2 FLOP x 2.4 GHz
 HBM_PEAK_GBS = 8000.0
 
 WORKLOADS = ("default", "tiny_f32", "prefill_4k", "varlen", "decode", "long_g4", "long_g1",
@@ -174,6 +174,12 @@ class Prefill:
     def peak(self):
         import workloads as W
         return FP32_PEAK_TFLOPS if self.case.dtype == W.F32 else MFMA_BF16_PEAK_TFLOPS
+
+    @property
+    def bound(self):
+        # the fp32 kernel's products run on the vector ALUs, the bf16 kernel's on the matrix cores
+        import workloads as W
+        return "alu" if self.case.dtype == W.F32 else "mfma"
 
 
 class PrefillCached:
@@ -346,7 +352,7 @@ def measure(runner, steps, warmup, workload_name):
         unit, peak, bound = "GB/s", HBM_PEAK_GBS, "hbm"
     else:
         rate = lambda ms: work / (ms * 1e-3) / 1e12  # noqa: E731
-        unit, peak, bound = "TFLOP/s", runner.peak, "mfma"
+        unit, peak, bound = "TFLOP/s", runner.peak, getattr(runner, "bound", "mfma")
     return {
         "workload": workload_name, "unit": unit, "work": work,
         "work_unit": "B" if unit == "GB/s" else "FLOP",

@@ -83,3 +83,12 @@ def test_cpu_baseline_leg_on_small_cases():
     assert per["varlen_x"]["scale"] == 4 and per["decode"]["unit"] == "GB/s"
     lens = np.sort(cases["decode"].seq_lens)
     assert abs(per["decode"]["scale"] - lens.sum() / lens[::4].sum()) < 1e-3
+
+
+@pytest.mark.parametrize("make,bound,peak", [(W.tiny_f32, "alu", bench.FP32_PEAK_TFLOPS),
+                                             (W.prefill_4k, "mfma", bench.MFMA_BF16_PEAK_TFLOPS)])
+def test_prefill_roofline_bound_follows_the_dtype(make, bound, peak):
+    # the fp32 kernel's products run on the vector ALUs, the bf16 kernel's on the matrix cores
+    r = object.__new__(bench.Prefill)
+    r.case = make()
+    assert r.bound == bound and r.peak == peak
