@@ -92,3 +92,27 @@ def test_prefill_roofline_bound_follows_the_dtype(make, bound, peak):
     r = object.__new__(bench.Prefill)
     r.case = make()
     assert r.bound == bound and r.peak == peak
+
+
+def _record_file(tmp_path, src_text, sha):
+    src = tmp_path / "k.hip"
+    src.write_text(src_text)
+    rec = tmp_path / "rec.md"
+    rec.write_text("```\n    record: kernel=kern workload=wl sources=k.hip sha256=" + sha +
+                   " fetch_kib=10.0 write_kib=4.0 fetch_factor=2.0000 write_factor=1.0000\n```\n")
+    return rec
+
+
+def test_traffic_record_is_used_only_while_the_sources_match(tmp_path, monkeypatch):
+    import hashlib
+    text = "kernel source\n"
+    rec = _record_file(tmp_path, text, hashlib.sha256(text.encode()).hexdigest())
+    monkeypatch.setattr(bench, "TRAFFIC_RECORDS", str(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    # FETCH_SIZE x 2 + WRITE_SIZE x 1, in KiB
+    assert bench.measured_traffic("kern", "wl") == (10.0 * 2.0 + 4.0 * 1.0) * 1024.0
+    assert bench.measured_traffic("kern", "other") is None
+    assert bench.measured_traffic("other", "wl") is None
+    (tmp_path / "k.hip").write_text(text + "// changed\n")
+    assert bench.measured_traffic("kern", "wl") is None
+
